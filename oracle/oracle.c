@@ -1,0 +1,476 @@
+/*
+ * oracle.c -- plain CPU oracle for the strict joint-attention path of a
+ * Qwen-Image-style MMDiT block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no source with the GPU library.
+ *
+ * Pages followed (cited by title and section):
+ *   [Roadmap]     "[RFC][Qwen-Image][CUDA/ROCm] WS1/WS2 kernel roadmap,
+ *                 ablation matrix and integration plan" (issue 386): the
+ *                 "Model contract" table (rows Streams, Text input, Q/K
+ *                 preprocessing, RoPE) and "Numerical requirements".
+ *   [Kernel list] "[RFC] [Qwen-Image] WS1 Single-GPU Kernel List": the
+ *                 "Kernel table" rows qk_rmsnorm, multi_axis_rope,
+ *                 joint_attn_qk_gemm, joint_attn_softmax, joint_attn_av_gemm.
+ *   [Gain note]   the comment thread of [Roadmap]: the Q/K norm carries a
+ *                 learned weight of 128 entries with eps 1e-6, so its
+ *                 backward produces both dx and the weight gradient.
+ *
+ * What is computed is the plain mathematical definition, not a replica of any
+ * tiling: RMSNorm with a learned gain, then a three-axis rotary embedding,
+ * then masked softmax attention over the concatenated [text, image] sequence,
+ * and the exact gradients of that composition.  Loops are sequential in
+ * ascending index order with accumulators of type `real`; OpenMP only splits
+ * independent rows, so results do not depend on the thread count.
+ *
+ * Build: ORACLE_REAL selects the arithmetic type.  `float` is the FP32 CPU
+ * reference that [Roadmap] "Numerical requirements" asks for; `double` is the
+ * same algorithm in FP64, used to pin it with finite differences.  Compile
+ * without fast math and with -ffp-contract=off.
+ *
+ * Readings where the pages are silent (each one is also listed, with its
+ * reason, in the repository's design notes):
+ *   - a single FP32->BF16 rounding, after norm, gain and rotation (the pages
+ *     allow one cast, at the kernel's declared output);
+ *   - interleaved rotation pairs (2k, 2k+1); pair k belongs to axis 0 for
+ *     k < 8, axis 1 for 8 <= k < 36, axis 2 otherwise;
+ *   - image token (row r, col c) of an h x w grid sits at
+ *     (0, r - ceil(h/2), c - ceil(w/2)); text token j sits at o+j on all three
+ *     axes with o = max(floor(h/2), floor(w/2));
+ *   - rotation angles are formed in FP64 and their cos/sin rounded once;
+ *   - every query row (padded text rows too) is computed; the mask is on keys;
+ *   - with two gain sets, set 0 is the text stream and set 1 the image stream.
+ */
+#include <math.h>
+#include <tgmath.h> /* sqrt/exp/log follow the type of `real` */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#ifndef ORACLE_REAL
+#define ORACLE_REAL float
+#endif
+typedef ORACLE_REAL real;
+
+enum { HD = 128, NPAIR = 64 };
+
+/* -------------------------------------------------------------------------
+ * Precision conversions.  BF16 is the top half of an IEEE binary32.
+ * ---------------------------------------------------------------------- */
+
+/* BF16 -> real: exact (every BF16 value is representable in binary32). */
+void oracle_bf16_widen(int64_t n, const uint16_t* in, real* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t u = (uint32_t)in[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    out[i] = (real)f;
+  }
+}
+
+/* real -> BF16 with round-to-nearest-even, one rounding of the real value.
+ * Written from the definition: keep 8 significant bits of the binary value
+ * (BF16 shares binary32's exponent range, so its subnormal spacing is
+ * 2^-133), round the rest to nearest with ties to even, overflow to inf. */
+static uint16_t bf16_rne(double x) {
+  if (isnan(x)) return (uint16_t)0x7FC0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  int e;
+  (void)frexp(a, &e);            /* a = m * 2^e, m in [0.5, 1) */
+  int ulp_exp = e - 8;           /* 8 significant bits */
+  if (ulp_exp < -133) ulp_exp = -133;
+  double q = ldexp(a, -ulp_exp); /* exact scaling */
+  double fl = floor(q);
+  double rem = q - fl;           /* exact */
+  double rq = fl;
+  if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) rq = fl + 1.0;
+  double r = ldexp(rq, ulp_exp);
+  if (r >= 0x1.0p128) return (uint16_t)(sign | 0x7F80); /* overflow */
+  float f = (float)r;            /* exact: r has <= 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+void oracle_cast_bf16(int64_t n, const real* in, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne((double)in[i]);
+}
+
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_real_bytes(void) { return (int)sizeof(real); }
+
+/* -------------------------------------------------------------------------
+ * Positions  [Roadmap, "Model contract", row RoPE: image indices are centred
+ * and text starts at max(h/2, w/2); Kernel list, row multi_axis_rope: text
+ * tokens lie on the diagonal of the grid].
+ * ---------------------------------------------------------------------- */
+void oracle_positions(int T_txt, int gh, int gw, int32_t* pos /* [S][3] */) {
+  int o = (gh / 2 > gw / 2) ? gh / 2 : gw / 2;
+  int ch = (gh + 1) / 2, cw = (gw + 1) / 2;
+  for (int j = 0; j < T_txt; ++j) {
+    pos[3 * j + 0] = o + j;
+    pos[3 * j + 1] = o + j;
+    pos[3 * j + 2] = o + j;
+  }
+  for (int t = 0; t < gh * gw; ++t) {
+    int row = t / gw, col = t % gw;
+    int32_t* p = pos + 3 * (int64_t)(T_txt + t);
+    p[0] = 0;
+    p[1] = row - ch;
+    p[2] = col - cw;
+  }
+}
+
+/* -------------------------------------------------------------------------
+ * Rotary embedding  [Roadmap, "Model contract", row RoPE: axes of 16, 56 and
+ * 56 channels, theta 10000].  Pair k rotates by angle
+ * p_axis * theta^(-2i/d_axis), i being the pair's index inside its axis.
+ * ---------------------------------------------------------------------- */
+static void pair_axis(int k, int* axis, int* i, int* d) {
+  if (k < 8) { *axis = 0; *i = k; *d = 16; }
+  else if (k < 36) { *axis = 1; *i = k - 8; *d = 56; }
+  else { *axis = 2; *i = k - 36; *d = 56; }
+}
+
+/* cos/sin of every pair's angle for one position triple. */
+static void rope_cos_sin(const int32_t* p, double theta, real* c, real* s) {
+  for (int k = 0; k < NPAIR; ++k) {
+    int axis, i, d;
+    pair_axis(k, &axis, &i, &d);
+    double omega = pow(theta, -2.0 * (double)i / (double)d);
+    double phi = (double)p[axis] * omega;
+    c[k] = (real)cos(phi);
+    s[k] = (real)sin(phi);
+  }
+}
+
+/* Rotate n_tok tokens x H heads of 128 by their positions (forward). */
+void oracle_rope_apply(int64_t n_tok, int H, const int32_t* pos, double theta,
+                       const real* y, real* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_tok; ++t) {
+    real c[NPAIR], s[NPAIR];
+    rope_cos_sin(pos + 3 * t, theta, c, s);
+    for (int h = 0; h < H; ++h) {
+      const real* a = y + (t * H + h) * HD;
+      real* b = out + (t * H + h) * HD;
+      for (int k = 0; k < NPAIR; ++k) {
+        real y0 = a[2 * k], y1 = a[2 * k + 1];
+        real p0 = y0 * c[k];
+        real p1 = y1 * s[k];
+        real p2 = y0 * s[k];
+        real p3 = y1 * c[k];
+        b[2 * k] = p0 - p1;
+        b[2 * k + 1] = p2 + p3;
+      }
+    }
+  }
+}
+
+/* -------------------------------------------------------------------------
+ * RMSNorm with learned gain  [Roadmap, "Model contract", row Q/K
+ * preprocessing: per-head RMSNorm with a learned gain, eps 1e-6, applied
+ * before the rotation; Gain note].
+ *   ms = (1/128) sum_c x_c^2 ;  r = 1/sqrt(ms + eps) ;  y_c = g_c * (x_c * r)
+ * ---------------------------------------------------------------------- */
+static real rms_rinv(const real* x, real eps) {
+  real ss = 0;
+  for (int c = 0; c < HD; ++c) {
+    real sq = x[c] * x[c];
+    ss = ss + sq;
+  }
+  real ms = ss / (real)HD;
+  real den = sqrt(ms + eps);
+  return (real)1 / den;
+}
+
+void oracle_rmsnorm(int64_t n_rows, const real* x, const real* gain, real eps,
+                    real* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const real* a = x + r * HD;
+    real rinv = rms_rinv(a, eps);
+    for (int c = 0; c < HD; ++c) {
+      real xh = a[c] * rinv;
+      y[r * HD + c] = gain[c] * xh;
+    }
+  }
+}
+
+/* Gain set used by token s: set 0 = text stream, set 1 = image stream. */
+static const real* gain_for(const real* gain, int gain_streams, int s, int T_txt) {
+  return (gain_streams == 2 && s >= T_txt) ? gain + HD : gain;
+}
+
+/* Full prologue: y = rope(g * rmsnorm(x)), pre-cast.  x, y: [B][S][H][128]. */
+void oracle_qknorm_rope(int B, int S, int H, int T_txt, int gh, int gw,
+                        const real* x, const real* gain, int gain_streams,
+                        double theta, real eps, real* y) {
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)S);
+  oracle_positions(T_txt, gh, gw, pos);
+  real* tmp = (real*)malloc(sizeof(real) * (size_t)S * H * HD);
+  for (int b = 0; b < B; ++b) {
+    const real* xb = x + (int64_t)b * S * H * HD;
+    real* yb = y + (int64_t)b * S * H * HD;
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+      const real* g = gain_for(gain, gain_streams, s, T_txt);
+      for (int h = 0; h < H; ++h) {
+        const real* a = xb + ((int64_t)s * H + h) * HD;
+        real* t = tmp + ((int64_t)s * H + h) * HD;
+        real rinv = rms_rinv(a, eps);
+        for (int c = 0; c < HD; ++c) {
+          real xh = a[c] * rinv;
+          t[c] = g[c] * xh;
+        }
+      }
+    }
+    oracle_rope_apply(S, H, pos, theta, tmp, yb);
+  }
+  free(tmp);
+  free(pos);
+}
+
+/* -------------------------------------------------------------------------
+ * Attention  [Kernel list, rows joint_attn_qk_gemm (scores are Q K^T scaled
+ * by 1/sqrt(d) over a sequence of T_txt + T_img tokens), joint_attn_softmax
+ * (softmax over the keys), joint_attn_av_gemm (weights times V); Roadmap,
+ * "Model contract", rows Streams (joint, non-causal, text before image) and
+ * Text input (padded prompts need a key mask)].  Valid keys of a row with text
+ * length L
+ * are j < L and T_txt <= j < S.  Per (batch, head) slice; q, k, v are the
+ * dense [S][128] rows of that slice.
+ * ---------------------------------------------------------------------- */
+static int key_valid(int j, int T_txt, int L) { return j < L || j >= T_txt; }
+static real softmax_scale(void) { return (real)(1.0 / sqrt((double)HD)); }
+
+static void scores_row(int S, int T_txt, int L, const real* qi, const real* k,
+                       real* srow) {
+  real sc = softmax_scale();
+  for (int j = 0; j < S; ++j) {
+    if (!key_valid(j, T_txt, L)) { srow[j] = 0; continue; }
+    const real* kj = k + (int64_t)j * HD;
+    real dot = 0;
+    for (int c = 0; c < HD; ++c) {
+      real pr = qi[c] * kj[c];
+      dot = dot + pr;
+    }
+    srow[j] = dot * sc;
+  }
+}
+
+/* Softmax of one score row over the valid keys; returns the row max and
+ * fills p (masked entries exactly 0) and *lse = m + log(sum exp(s - m)). */
+static void softmax_row(int S, int T_txt, int L, const real* srow, real* p,
+                        real* lse) {
+  real m = -INFINITY;
+  for (int j = 0; j < S; ++j)
+    if (key_valid(j, T_txt, L) && srow[j] > m) m = srow[j];
+  real l = 0;
+  for (int j = 0; j < S; ++j) {
+    if (!key_valid(j, T_txt, L)) { p[j] = 0; continue; }
+    p[j] = exp(srow[j] - m);
+    l = l + p[j];
+  }
+  for (int j = 0; j < S; ++j) p[j] = p[j] / l;
+  *lse = m + log(l);
+}
+
+/* Forward for query rows [s0, s1): o [s1-s0][128] pre-cast, lse [s1-s0]. */
+void oracle_attn_fwd_bh(int S, int T_txt, int L, const real* q, const real* k,
+                        const real* v, int s0, int s1, real* o, real* lse) {
+#pragma omp parallel
+  {
+    real* srow = (real*)malloc(sizeof(real) * (size_t)S);
+    real* p = (real*)malloc(sizeof(real) * (size_t)S);
+#pragma omp for schedule(static)
+    for (int i = s0; i < s1; ++i) {
+      scores_row(S, T_txt, L, q + (int64_t)i * HD, k, srow);
+      softmax_row(S, T_txt, L, srow, p, &lse[i - s0]);
+      real acc[HD];
+      for (int c = 0; c < HD; ++c) acc[c] = 0;
+      for (int j = 0; j < S; ++j) {
+        if (!key_valid(j, T_txt, L)) continue;
+        const real* vj = v + (int64_t)j * HD;
+        for (int c = 0; c < HD; ++c) {
+          real pr = p[j] * vj[c];
+          acc[c] = acc[c] + pr;
+        }
+      }
+      for (int c = 0; c < HD; ++c) o[(int64_t)(i - s0) * HD + c] = acc[c];
+    }
+    free(p);
+    free(srow);
+  }
+}
+
+/* Gradients of the attention slice for upstream dO ([S][128]):
+ *   dP = dO V^T ; D_i = sum_c dO_ic O_ic ; dS = P o (dP - D) ;
+ *   dq = dS K / sqrt(d) ; dk = dS^T Q / sqrt(d) ; dv = P^T dO.
+ * O here is the oracle's own (pre-cast) output.  Masked keys get dk = dv = 0.
+ * P and dS are materialised ([S][S] each) so both reductions use the same
+ * values; columns are then summed in ascending query order. */
+int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
+                       const real* v, const real* dO, real* dq, real* dk,
+                       real* dv) {
+  real* P = (real*)malloc(sizeof(real) * (size_t)S * S);
+  real* dS = (real*)malloc(sizeof(real) * (size_t)S * S);
+  if (!P || !dS) { free(P); free(dS); return 1; }
+  real sc = softmax_scale();
+#pragma omp parallel
+  {
+    real* srow = (real*)malloc(sizeof(real) * (size_t)S);
+#pragma omp for schedule(static)
+    for (int i = 0; i < S; ++i) {
+      real lse;
+      real* p = P + (int64_t)i * S;
+      scores_row(S, T_txt, L, q + (int64_t)i * HD, k, srow);
+      softmax_row(S, T_txt, L, srow, p, &lse);
+      real oi[HD];
+      for (int c = 0; c < HD; ++c) oi[c] = 0;
+      for (int j = 0; j < S; ++j) {
+        if (!key_valid(j, T_txt, L)) continue;
+        for (int c = 0; c < HD; ++c) {
+          real pr = p[j] * v[(int64_t)j * HD + c];
+          oi[c] = oi[c] + pr;
+        }
+      }
+      const real* g = dO + (int64_t)i * HD;
+      real Di = 0;
+      for (int c = 0; c < HD; ++c) {
+        real pr = g[c] * oi[c];
+        Di = Di + pr;
+      }
+      real* ds = dS + (int64_t)i * S;
+      for (int j = 0; j < S; ++j) {
+        if (!key_valid(j, T_txt, L)) { ds[j] = 0; continue; }
+        real dp = 0;
+        for (int c = 0; c < HD; ++c) {
+          real pr = g[c] * v[(int64_t)j * HD + c];
+          dp = dp + pr;
+        }
+        ds[j] = p[j] * (dp - Di);
+      }
+      for (int c = 0; c < HD; ++c) {
+        real acc = 0;
+        for (int j = 0; j < S; ++j) {
+          if (!key_valid(j, T_txt, L)) continue;
+          real pr = ds[j] * k[(int64_t)j * HD + c];
+          acc = acc + pr;
+        }
+        dq[(int64_t)i * HD + c] = acc * sc;
+      }
+    }
+    free(srow);
+  }
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < S; ++j) {
+    real* dkj = dk + (int64_t)j * HD;
+    real* dvj = dv + (int64_t)j * HD;
+    if (!key_valid(j, T_txt, L)) {
+      for (int c = 0; c < HD; ++c) { dkj[c] = 0; dvj[c] = 0; }
+      continue;
+    }
+    for (int c = 0; c < HD; ++c) {
+      real ak = 0, av = 0;
+      for (int i = 0; i < S; ++i) {
+        real pk = dS[(int64_t)i * S + j] * q[(int64_t)i * HD + c];
+        ak = ak + pk;
+        real pv = P[(int64_t)i * S + j] * dO[(int64_t)i * HD + c];
+        av = av + pv;
+      }
+      dkj[c] = ak * sc;
+      dvj[c] = av;
+    }
+  }
+  free(P);
+  free(dS);
+  return 0;
+}
+
+/* -------------------------------------------------------------------------
+ * Prologue backward  [Gain note; Roadmap, "Work items": every differentiable
+ * operator comes with a forward and a backward].  For each row with upstream dy (gradient of the
+ * rotated, pre-cast output; the single output cast is treated as identity):
+ *   u = R^T dy ; dg += u o xhat ; dxhat = u o g ;
+ *   dx = r * (dxhat - xhat * (1/128) sum_c dxhat_c xhat_c).
+ * dg is per sample and per gain set: dg_per_sample [B][gain_streams][128],
+ * each entry summed over (s, h) in ascending order.
+ * ---------------------------------------------------------------------- */
+void oracle_qknorm_rope_bwd(int B, int S, int H, int T_txt, int gh, int gw,
+                            const real* x, const real* gain, int gain_streams,
+                            double theta, real eps, const real* dy, real* dx,
+                            real* dg_per_sample) {
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)S);
+  oracle_positions(T_txt, gh, gw, pos);
+  int64_t rows = (int64_t)S * H;
+  real* U = (real*)malloc(sizeof(real) * (size_t)rows * HD);
+  real* XH = (real*)malloc(sizeof(real) * (size_t)rows * HD);
+  for (int b = 0; b < B; ++b) {
+    const real* xb = x + (int64_t)b * rows * HD;
+    const real* dyb = dy + (int64_t)b * rows * HD;
+    real* dxb = dx + (int64_t)b * rows * HD;
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+      real c[NPAIR], sn[NPAIR];
+      rope_cos_sin(pos + 3 * (int64_t)s, theta, c, sn);
+      const real* g = gain_for(gain, gain_streams, s, T_txt);
+      for (int h = 0; h < H; ++h) {
+        int64_t r = (int64_t)s * H + h;
+        const real* a = xb + r * HD;
+        const real* d = dyb + r * HD;
+        real* u = U + r * HD;
+        real* xh = XH + r * HD;
+        for (int k = 0; k < NPAIR; ++k) {
+          real d0 = d[2 * k], d1 = d[2 * k + 1];
+          real p0 = d0 * c[k];
+          real p1 = d1 * sn[k];
+          real p2 = d0 * sn[k];
+          real p3 = d1 * c[k];
+          u[2 * k] = p0 + p1;
+          u[2 * k + 1] = p3 - p2;
+        }
+        real rinv = rms_rinv(a, eps);
+        for (int cc = 0; cc < HD; ++cc) xh[cc] = a[cc] * rinv;
+        real dot = 0;
+        real dxh[HD];
+        for (int cc = 0; cc < HD; ++cc) {
+          dxh[cc] = u[cc] * g[cc];
+          real pr = dxh[cc] * xh[cc];
+          dot = dot + pr;
+        }
+        real mean = dot / (real)HD;
+        for (int cc = 0; cc < HD; ++cc) {
+          real t = xh[cc] * mean;
+          dxb[r * HD + cc] = rinv * (dxh[cc] - t);
+        }
+      }
+    }
+    /* dg for this sample: ascending (s, h) per channel and gain set. */
+    for (int st = 0; st < gain_streams; ++st) {
+      real* dg = dg_per_sample + ((int64_t)b * gain_streams + st) * HD;
+#pragma omp parallel for schedule(static)
+      for (int cc = 0; cc < HD; ++cc) {
+        real acc = 0;
+        for (int s = 0; s < S; ++s) {
+          int set = (gain_streams == 2 && s >= T_txt) ? 1 : 0;
+          if (set != st) continue;
+          for (int h = 0; h < H; ++h) {
+            int64_t r = (int64_t)s * H + h;
+            real pr = U[r * HD + cc] * XH[r * HD + cc];
+            acc = acc + pr;
+          }
+        }
+        dg[cc] = acc;
+      }
+    }
+  }
+  free(XH);
+  free(U);
+  free(pos);
+}

@@ -1,0 +1,108 @@
+"""Seeded synthetic workloads for the strict joint-attention path.
+
+This module holds the workload shapes and the seeded input generators shared
+by the GPU tests, the oracle tests and the benchmark.  It performs none of the
+method's arithmetic: it only draws random tensors and describes geometry.
+
+Shapes follow the pages' reference resolutions (the "Model contract" table of
+the Qwen-Image roadmap RFC, row "Reference shapes": 1024x1024, 1328x1328 and
+1664x928 pixels, i.e. 64x64, 83x83 and 104x58 image tokens after the 16x
+reduction of the latent packing) with 24 heads of 128 channels.  The pages use
+checkpoint activations; none are available, so Q, K, V and dO are standard
+normal BF16 draws and the RMSNorm gains are FP32 draws around 1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+HEAD_DIM = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T_txt: int
+    txt_len: tuple
+    h: int
+    w: int
+    seed: int
+    backward: bool = False
+    note: str = ""
+
+    @property
+    def T_img(self) -> int:
+        return self.h * self.w
+
+    @property
+    def S(self) -> int:
+        return self.T_txt + self.h * self.w
+
+    def valid_keys(self) -> list:
+        return [L + self.T_img for L in self.txt_len]
+
+    def fwd_flops(self) -> float:
+        """Algorithmic forward FLOPs: 2 GEMMs of 2*S*K*D per (b, h)."""
+        return float(sum(4 * HEAD_DIM * self.H * self.S * K for K in self.valid_keys()))
+
+    def bwd_flops(self) -> float:
+        """Algorithmic backward FLOPs: 5 GEMMs of 2*S*K*D per (b, h)."""
+        return float(sum(10 * HEAD_DIM * self.H * self.S * K for K in self.valid_keys()))
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 8, (5,), 4, 4, 0, note="B=1, 2x128, T_txt=8 (5 valid), 4x4 grid"),
+    "1024sq": Workload("1024sq", 1, 24, 256, (219,), 64, 64, 1, note="1024^2 image, single sample"),
+    "1328sq_cfg": Workload("1328sq_cfg", 2, 24, 512, (301, 12), 83, 83, 2, note="1328^2 CFG pair"),
+    "1664x928": Workload("1664x928", 4, 24, 512, (7, 64, 200, 511), 104, 58, 3,
+                         note="1664x928 batch-invariance sweep"),
+    "1024sq_bwd": Workload("1024sq_bwd", 1, 24, 256, (219,), 64, 64, 4, backward=True,
+                           note="deterministic backward at 1024^2"),
+}
+
+
+def make_inputs(wl: Workload, extra_samples: int = 0, gain_mean: float = 1.0, gain_std: float = 0.1,
+                gain_streams: int = 1) -> dict:
+    """Draw the workload's inputs on the CPU from its seed.
+
+    Draw order: Q, K, V as N(0,1) rounded to BF16, then g_q and g_k as
+    gain_mean + gain_std * N(0,1) in FP32, then dO (backward workloads).
+    ``extra_samples`` appends further batch rows drawn next from the same
+    generator (same shapes, text length of the last row)."""
+    g = torch.Generator("cpu").manual_seed(wl.seed)
+    B, S, H = wl.B, wl.S, wl.H
+
+    def bf16(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+    q, k, v = bf16(B, S, H, HEAD_DIM), bf16(B, S, H, HEAD_DIM), bf16(B, S, H, HEAD_DIM)
+    gq = gain_mean + gain_std * torch.randn(gain_streams, HEAD_DIM, generator=g, dtype=torch.float32)
+    gk = gain_mean + gain_std * torch.randn(gain_streams, HEAD_DIM, generator=g, dtype=torch.float32)
+    dO = bf16(B, S, H, HEAD_DIM) if wl.backward else None
+    txt_len = list(wl.txt_len)
+    if extra_samples:
+        qs, ks, vs, ds = [q], [k], [v], [dO]
+        for _ in range(extra_samples):
+            qs.append(bf16(1, S, H, HEAD_DIM))
+            ks.append(bf16(1, S, H, HEAD_DIM))
+            vs.append(bf16(1, S, H, HEAD_DIM))
+            if wl.backward:
+                ds.append(bf16(1, S, H, HEAD_DIM))
+            txt_len.append(txt_len[-1])
+        q, k, v = torch.cat(qs), torch.cat(ks), torch.cat(vs)
+        dO = torch.cat(ds) if wl.backward else None
+    return dict(q=q, k=k, v=v, g_q=gq, g_k=gk, dO=dO, txt_len=txt_len, T_txt=wl.T_txt, h=wl.h, w=wl.w)
+
+
+def custom(name: str, B: int, H: int, T_txt: int, txt_len, h: int, w: int, seed: int,
+           backward: bool = False) -> Workload:
+    """A workload with explicit geometry (tests of ragged and edge shapes)."""
+    return Workload(name, B, H, T_txt, tuple(txt_len), h, w, seed, backward)
+
+
+def bits(t: torch.Tensor):
+    """BF16 tensor -> numpy uint16 bit patterns (a view, no arithmetic)."""
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
