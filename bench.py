@@ -1,0 +1,218 @@
+"""Benchmark of the strict joint-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024sq]
+
+A step is one pass of the path over one batch of synthetic input that is
+already resident in HBM: the Q and K prologues (RMSNorm + gain + RoPE) and
+the attention forward; for a backward workload the step also runs the
+backward (attention + prologue gradients).  Prints ONE JSON line.
+
+value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
+with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).
+The attention-forward kernel is also timed alone with HIP events on the
+launch stream; that time gives the roofline fraction against the MI355X
+dense BF16 MFMA peak (2.5 PFLOP/s).  The CPU oracle is timed on a bounded
+sample of the same workload on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="1024sq")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "invariant_joint_attention_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, src: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != source_hash(src):
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the path shards over (batch, head) with no exchange, "
+              "and this build measures one GPU's share; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import invariant_joint_attention_amd as qi
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = workloads.make_inputs(wl)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    geo = qi.Geometry(B=wl.B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w, txt_len=list(wl.txt_len))
+    qi.strict_probe(0)
+
+    # preallocated outputs: the timed region launches kernels only
+    shp = g["q"].shape
+    qp = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    kp = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.B, wl.H, wl.S), dtype=torch.float32, device=dev)
+    of = torch.empty(shp, dtype=torch.float32, device=dev) if wl.backward else None
+    if wl.backward:
+        ws = torch.empty(qi.bwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
+        grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
+
+    ev = {n: [] for n in ("pro", "fwd", "bwd")}
+
+    def step(timed: bool):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if timed:
+            e[0].record()
+        qi.qknorm_rope(g["q"], g["g_q"], geo, out=qp)
+        qi.qknorm_rope(g["k"], g["g_k"], geo, out=kp)
+        if timed:
+            e[1].record()
+        qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of)
+        if timed:
+            e[2].record()
+        if wl.backward:
+            qi.joint_attn_bwd(g["q"], g["k"], qp, kp, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo,
+                              workspace=ws, **grads)
+        if timed:
+            e[3].record()
+            ev["pro"].append((e[0], e[1]))
+            ev["fwd"].append((e[1], e[2]))
+            ev["bwd"].append((e[2], e[3]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def avg_ms(name):
+        return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
+
+    pro_ms, fwd_ms, bwd_ms = avg_ms("pro"), avg_ms("fwd"), avg_ms("bwd")
+    fwd_flops = wl.fwd_flops()
+    value = fwd_flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    pro_bytes = 2 * 2 * 2 * wl.B * wl.S * wl.H * 128  # Q and K, read + write BF16
+
+    traffic = traffic_from_profile("attn_fwd_kernel", "qi_attn_fwd.hip", args.workload)
+    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "flops_per_launch": fwd_flops, "avg_launch_ms": round(fwd_ms, 4)}
+
+    out = {
+        "metric": "joint-attn fwd TFLOP/s and % BF16 MFMA peak at 1024^2 (S=4096+256), 24x128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "B": wl.B, "heads": wl.H, "head_dim": 128,
+                   "T_txt": wl.T_txt, "txt_len": list(wl.txt_len), "grid": [wl.h, wl.w], "S": wl.S,
+                   "backward": wl.backward},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "attn_fwd": {"ms": round(fwd_ms, 4), "tflops": round(attn_tflops, 2),
+                     "pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2)},
+        "prologue_qk": {"ms": round(pro_ms, 4), "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "roofline": roofline,
+    }
+    if wl.backward:
+        bflops = wl.bwd_flops()
+        out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
+                           "algorithmic_flops": bflops}
+
+    # ---------------------------------------------------------- CPU baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, qp, kp, o, lse, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, qp, kp, o, lse, target_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload:
+    the attention forward of every query row of the first heads, on all
+    host threads; also checks those rows against the GPU output."""
+    import numpy as np
+
+    from oracle import Oracle
+
+    orc = Oracle("f32")
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    orc.set_threads(threads)
+    f = lambda t: t.detach().float().cpu().numpy()  # noqa: E731
+    qn, kn, vn, on, ln = f(qp), f(kp), f(inp["v"]), f(o), f(lse)
+    K0 = wl.valid_keys()[0]
+    flops_per_row = 4.0 * 128 * K0
+    # calibrate on 64 rows, then size the sample to about target_s seconds
+    t = time.perf_counter()
+    orc.attn_fwd_bh(qn[0, :, 0], kn[0, :, 0], vn[0, :, 0], wl.T_txt, wl.txt_len[0], 0, 64)
+    per_row = (time.perf_counter() - t) / 64
+    n_rows = int(max(64, min(wl.S * wl.H, target_s / max(per_row, 1e-9))))
+    done, worst, flops, t_cpu = 0, 0.0, 0.0, 0.0
+    h = 0
+    while done < n_rows and h < wl.H:
+        rows = min(wl.S, n_rows - done)
+        t = time.perf_counter()
+        ro, rl = orc.attn_fwd_bh(qn[0, :, h], kn[0, :, h], vn[0, :, h], wl.T_txt, wl.txt_len[0], 0, rows)
+        t_cpu += time.perf_counter() - t
+        flops += flops_per_row * rows
+        err = np.abs(on[0, :rows, h].astype(np.float64) - ro)
+        worst = max(worst, float(np.max(err / (1e-2 * np.abs(ro) + 2e-3))))
+        done += rows
+        h += 1
+    return {"value": round(flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"attention forward of {done} query rows (heads 0..{h - 1} of batch row 0, all "
+                      f"{K0} valid keys each) of the same workload, FP32 C oracle, {t_cpu:.1f} s",
+            "seconds": round(t_cpu, 2),
+            "sample_parity_max_ratio_to_bound": round(worst, 4)}
+
+
+if __name__ == "__main__":
+    main()

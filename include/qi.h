@@ -1,0 +1,194 @@
+/*
+ * qi.h -- C ABI of the strict joint-attention library for AMD Instinct
+ * MI355X (gfx950): learned-gain Q/K RMSNorm + three-axis RoPE, and masked
+ * non-causal joint attention over [text, image] with a deterministic
+ * backward.
+ *
+ * Pages cited (by title and section):
+ *   [Roadmap]     "[RFC][Qwen-Image][CUDA/ROCm] WS1/WS2 kernel roadmap,
+ *                 ablation matrix and integration plan" (issue 386).
+ *   [Kernel list] "[RFC] [Qwen-Image] WS1 Single-GPU Kernel List".
+ *   [PR 537]      "[WS1][Qwen-Image][CUDA] AdaLN modulation projection
+ *                 (adaln_mod_projection)".
+ *   [PR 507]      "[WS1][CUDA][Qwen3-Next] TP4 GDN, convolution and D=256
+ *                 attention mixers on real weights".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory.  Every tensor pointer is a DEVICE pointer owned by the caller;
+ *    `txt_len` in qi_geom is a HOST array.  The library never allocates,
+ *    frees or retains a pointer after the call returns, and never writes an
+ *    input.  Work is enqueued on `stream` (0 = the default stream); calls
+ *    return without synchronising.
+ *  - Activations are [B, S, H, 128] views (qi_bshd): the head-dim stride is 1
+ *    and B, S, H strides are given in elements.  The sequence axis is the
+ *    concatenation [text (T_txt, padded), image (grid_h * grid_w tokens,
+ *    row-major)] ([Roadmap], "Model contract", row Streams).
+ *  - Alignment: every data pointer 16-byte aligned and every stride a
+ *    multiple of 16 bytes ([PR 537], the input-check rule of its kernel).
+ *  - Status.  0 on success, else one of the QI_E_* codes; qi_last_error()
+ *    then holds a message for the calling thread.  All arguments are
+ *    validated before anything is launched: a failed call writes nothing.
+ *    Configurations outside the strict contract fail closed ([Roadmap],
+ *    "Numerical requirements"; [Kernel list], the rule against silent
+ *    fallback): there is no other code path.
+ *  - Determinism.  Fixed reduction trees, FP32 accumulation, no split-KV /
+ *    Split-K / atomics; a row's output bytes do not depend on batch size,
+ *    batch position, text padding, launch geometry or repetition
+ *    ([Roadmap], "Numerical requirements"; [Kernel list], rules 1-6).
+ */
+#ifndef QI_H
+#define QI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QI_HEAD_DIM 128
+
+enum qi_status {
+  QI_OK = 0,
+  QI_E_INVALID = 1,     /* null pointer, bad size or geometry, txt_len out of range */
+  QI_E_UNSUPPORTED = 2, /* D != 128, RoPE axes != {16,56,56}, no gfx950 device */
+  QI_E_ALIGN = 3,       /* pointer or stride not 16-byte aligned */
+  QI_E_ALIAS = 4,       /* an output overlaps an input or another output */
+  QI_E_WORKSPACE = 5,   /* workspace null or smaller than qi_joint_attn_bwd_workspace() */
+  QI_E_STRICT = 6,      /* strict-arithmetic probe failed on the device */
+  QI_E_HIP = 7          /* a HIP runtime call or launch failed */
+};
+
+/* A [B, S, H, 128] view; element type given by the entry point. */
+typedef struct {
+  void* data;
+  int64_t sb, ss, sh; /* strides in elements; the head-dim stride is 1 */
+} qi_bshd;
+
+/* Geometry of one call ([Roadmap], "Model contract": 24 heads x 128, text
+ * length padded with a key mask, image grid of the reference shapes). */
+typedef struct {
+  int32_t B;              /* batch rows, >= 1 */
+  int32_t H;              /* heads, >= 1 */
+  int32_t D;              /* head dim; must be 128 */
+  int32_t T_txt;          /* padded text length, >= 0 */
+  int32_t grid_h, grid_w; /* image token grid, each >= 1; S = T_txt + grid_h*grid_w */
+  const int32_t* txt_len; /* HOST [B]: valid text length of each row, 0..T_txt */
+  int32_t rope_axes[3];   /* must be {16, 56, 56} */
+  double rope_theta;      /* finite, > 1 (the model uses 10000) */
+  float rms_eps;          /* finite, > 0 (the model uses 1e-6) */
+  int32_t gain_streams;   /* 1: one [128] gain for all tokens; 2: [2][128],
+                             set 0 for text tokens, set 1 for image tokens */
+} qi_geom;
+
+/*
+ * qi_qknorm_rope -- prologue: per-head RMSNorm with a learned gain, then the
+ * three-axis rotary embedding, then one FP32->BF16 rounding.
+ *   [Roadmap] "Model contract", rows Q/K preprocessing (RMSNorm with learned
+ *   gain, eps, before RoPE) and RoPE (axes 16/56/56, theta, centred image
+ *   indices, text offset max(h/2, w/2)); [Kernel list] rows qk_rmsnorm and
+ *   multi_axis_rope (text on the grid diagonal).
+ * For each (b, s, h) row x of 128 BF16 values:
+ *   r = 1/sqrt(mean(x^2) + eps);  t = gain ⊙ (x * r);
+ *   y = bf16_rne(rotate(t)), pairs (2k, 2k+1) rotated by p_axis(k) * omega_k,
+ *   positions: image token (row i, col j) -> (0, i - ceil(h/2), j - ceil(w/2)),
+ *   text token j -> (o+j, o+j, o+j) with o = max(floor(h/2), floor(w/2)).
+ * Arguments:
+ *   x        BF16 [B,S,H,128] input (Q or K from the projection).
+ *   gain     FP32 device [gain_streams][128].
+ *   y        BF16 [B,S,H,128] output; must not overlap x or gain.
+ *   y_f32    nullable FP32 dense [B,S,H,128] output of the pre-cast values.
+ */
+int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
+                   float* y_f32, hipStream_t stream);
+
+/*
+ * qi_joint_attn_fwd -- masked non-causal attention over [text, image].
+ *   [Kernel list] rows joint_attn_qk_gemm, joint_attn_softmax,
+ *   joint_attn_av_gemm and joint_attention_fused; [Roadmap] "Model
+ *   contract", rows Streams and Text input (key mask for padded prompts).
+ * Row b attends to keys j < txt_len[b] and T_txt <= j < S; every query row,
+ * padded text rows included, is computed.
+ *   O[b,i,h,:] = bf16_rne( sum_j softmax_j(q_i . k_j / sqrt(128)) v_j )
+ *   lse[b,h,i] = ln sum_j exp(q_i . k_j / sqrt(128))   (FP32)
+ * Arguments:
+ *   q, k, v  BF16 [B,S,H,128] (q, k are the prologue outputs).
+ *   o        BF16 [B,S,H,128] output.
+ *   lse      FP32 dense [B,H,S] output (kept for the backward).
+ *   o_f32    nullable FP32 dense [B,S,H,128] output of the pre-cast O; the
+ *            backward needs it.
+ * P enters the A.V product as two BF16 terms (hi = bf16(p), lo = bf16(p-hi))
+ * so the output meets 1e-2*|ref| + 2e-3 even where O cancels on a few
+ * peaked keys; the row sum uses the FP32 p.
+ */
+int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o,
+                      float* lse, float* o_f32, hipStream_t stream);
+
+/* Bytes of device workspace qi_joint_attn_bwd needs for this geometry. */
+size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
+
+/*
+ * qi_joint_attn_bwd -- gradients of the whole path (attention, rotation,
+ * RMSNorm and gains) for upstream dO, with fixed-order tile sums and no
+ * atomics ([Roadmap], "Work items": every differentiable operator has a
+ * backward; "Numerical requirements"; the learned-gain comment of [Roadmap]
+ * whose backward yields both dx and the gain gradient).
+ *   dP = dO V^T;  D_i = dO_i . O_i;  dS = P ⊙ (dP - D);
+ *   dq' = dS K / sqrt(128);  dk' = dS^T Q / sqrt(128);  dv = P^T dO;
+ *   then for q (and likewise k): u = R^T dq';  dgain += u ⊙ xhat;
+ *   dx = r (u ⊙ g - xhat * mean(u ⊙ g ⊙ xhat)).
+ * Arguments:
+ *   q_raw, k_raw   BF16 [B,S,H,128] prologue inputs.
+ *   q, k, v        BF16 [B,S,H,128] prologue outputs and V.
+ *   o_f32          FP32 [B,S,H,128]: the forward's pre-cast O (the o_f32
+ *                  output of qi_joint_attn_fwd).  D_i is formed from it: the
+ *                  BF16 O would shift D by ~2^-9 |dO||O| sqrt(128), more than
+ *                  the gain gradients tolerate.
+ *   lse            FP32 dense [B,H,S] from the forward.
+ *   d_o            BF16 [B,S,H,128] upstream gradient.
+ *   gain_q, gain_k FP32 device [gain_streams][128].
+ *   dq, dk, dv     FP32 [B,S,H,128] outputs (dq, dk w.r.t. q_raw, k_raw).
+ *   dgain_q_ps, dgain_k_ps   FP32 device [B][gain_streams][128]: gain
+ *                  gradients of each sample alone.
+ *   dgain_q, dgain_k  nullable FP32 device [gain_streams][128]: the
+ *                  per-sample values summed in ascending b.
+ *   workspace      device buffer of at least qi_joint_attn_bwd_workspace()
+ *                  bytes, 256-byte aligned; its contents are scratch.
+ */
+int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd q,
+                      qi_bshd k, qi_bshd v, qi_bshd o_f32, const float* lse, qi_bshd d_o,
+                      const float* gain_q, const float* gain_k, qi_bshd dq, qi_bshd dk,
+                      qi_bshd dv, float* dgain_q_ps, float* dgain_k_ps, float* dgain_q,
+                      float* dgain_k, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Message for the calling thread's last nonzero status ("" if none). */
+const char* qi_last_error(void);
+
+/*
+ * qi_strict_probe -- run the strict-arithmetic probe kernel on `device`:
+ * an FP32 subnormal must survive a multiply, a division and a square root
+ * must be correctly rounded, and the library's FP32->BF16 cast must round to
+ * nearest even (cf. [PR 537], its probe of the built arithmetic).  The
+ * verdict is cached per device id.  Returns QI_OK or QI_E_STRICT (or
+ * QI_E_UNSUPPORTED / QI_E_HIP when the device cannot run it).
+ */
+int qi_strict_probe(int device);
+
+/*
+ * qi_trace -- JSON text describing the arithmetic contract the library was
+ * built with: kernel names, frozen tile sizes, MFMA instructions, reduction
+ * orders, accumulator precision, split-K / split-KV / atomics state, build
+ * flags and target ([Kernel list], rule 7; [Roadmap], "Work items",
+ * qwenimage_operator_trace).  The string is static; do not free it.
+ */
+const char* qi_trace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI_H */

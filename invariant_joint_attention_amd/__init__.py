@@ -1,0 +1,192 @@
+"""Strict joint attention for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libqi.so`` (declared in ``include/qi.h``).  It only
+marshals arguments: every step of the path -- the learned-gain Q/K RMSNorm
+with three-axis RoPE, the masked joint attention forward and its
+deterministic backward -- runs in the library's HIP kernels.  torch supplies
+device memory and the current stream.  A nonzero status raises ``QiError``;
+there is no other code path, and a missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HEAD_DIM = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqi.so")
+
+STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN", 4: "QI_E_ALIAS",
+          5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
+
+# every entry point declared in include/qi.h
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_bwd_workspace", "qi_joint_attn_bwd",
+           "qi_last_error", "qi_strict_probe", "qi_trace")
+
+
+class QiError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class QiBshd(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("sb", ctypes.c_int64), ("ss", ctypes.c_int64), ("sh", ctypes.c_int64)]
+
+
+class QiGeom(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("T_txt", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("txt_len", ctypes.POINTER(ctypes.c_int32)), ("rope_axes", ctypes.c_int32 * 3),
+                ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float), ("gain_streams", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with invariant_joint_attention_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, G, S = ctypes.c_void_p, ctypes.POINTER(QiGeom), ctypes.c_void_p
+        L.qi_qknorm_rope.argtypes = [G, QiBshd, P, QiBshd, P, S]
+        L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, S]
+        L.qi_joint_attn_bwd_workspace.argtypes = [G]
+        L.qi_joint_attn_bwd_workspace.restype = ctypes.c_size_t
+        L.qi_joint_attn_bwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, P, QiBshd, P, P,
+                                        QiBshd, QiBshd, QiBshd, P, P, P, P, P, ctypes.c_size_t, S]
+        L.qi_last_error.restype = ctypes.c_char_p
+        L.qi_strict_probe.argtypes = [ctypes.c_int]
+        L.qi_trace.restype = ctypes.c_char_p
+        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_bwd", "qi_strict_probe"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise QiError(rc, lib().qi_last_error().decode())
+
+
+class Geometry:
+    """Geometry of one call (mirrors ``qi_geom``)."""
+
+    def __init__(self, B, H, T_txt, grid_h, grid_w, txt_len, rope_theta=10000.0, rms_eps=1e-6, gain_streams=1,
+                 D=HEAD_DIM, rope_axes=(16, 56, 56)):
+        self.B, self.H, self.T_txt, self.grid_h, self.grid_w = int(B), int(H), int(T_txt), int(grid_h), int(grid_w)
+        self.txt_len = [int(x) for x in txt_len]
+        self.S = self.T_txt + self.grid_h * self.grid_w
+        self._len = (ctypes.c_int32 * max(1, len(self.txt_len)))(*self.txt_len)
+        self.c = QiGeom(self.B, self.H, int(D), self.T_txt, self.grid_h, self.grid_w,
+                        ctypes.cast(self._len, ctypes.POINTER(ctypes.c_int32)),
+                        (ctypes.c_int32 * 3)(*rope_axes), float(rope_theta), float(rms_eps), int(gain_streams))
+        self.gain_streams = int(gain_streams)
+
+    def ptr(self):
+        return ctypes.byref(self.c)
+
+
+def _bshd(t: torch.Tensor) -> QiBshd:
+    if t.dim() != 4:
+        raise ValueError("expected a [B, S, H, 128] tensor")
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must have stride 1")
+    return QiBshd(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    return t.data_ptr()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def qknorm_rope(x, gain, geom: Geometry, out=None, out_f32=None):
+    """y = bf16(rope(gain * rmsnorm(x))) for a BF16 [B,S,H,128] tensor."""
+    if out is None:
+        out = _empty(x.shape, torch.bfloat16, x)
+    _check(lib().qi_qknorm_rope(geom.ptr(), _bshd(x), _ptr(gain), _bshd(out), _ptr(out_f32), _stream()))
+    return out
+
+
+def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None):
+    """Masked joint attention forward; returns (O BF16 [B,S,H,128], LSE FP32 [B,H,S])."""
+    if out is None:
+        out = _empty(q.shape, torch.bfloat16, q)
+    if lse is None:
+        lse = _empty((geom.B, geom.H, geom.S), torch.float32, q)
+    _check(lib().qi_joint_attn_fwd(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
+                                   _ptr(out_f32), _stream()))
+    return out, lse
+
+
+def bwd_workspace_bytes(geom: Geometry) -> int:
+    return int(lib().qi_joint_attn_bwd_workspace(geom.ptr()))
+
+
+def joint_attn_bwd(q_raw, k_raw, q, k, v, o_f32, lse, d_o, gain_q, gain_k, geom: Geometry, workspace=None,
+                   dq=None, dk=None, dv=None):
+    """Gradients of the whole path (o_f32: the forward's FP32 pre-cast O).
+    Returns a dict with dq, dk, dv (FP32
+    [B,S,H,128], w.r.t. the raw prologue inputs and V), dgain_q_ps /
+    dgain_k_ps (FP32 [B, gain_streams, 128]) and dgain_q / dgain_k (their
+    sums in ascending batch order)."""
+    dev = q.device
+    shp = q.shape
+    dq = torch.empty(shp, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty(shp, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty(shp, dtype=torch.float32, device=dev) if dv is None else dv
+    ns = geom.gain_streams
+    dgq_ps = torch.empty((geom.B, ns, HEAD_DIM), dtype=torch.float32, device=dev)
+    dgk_ps = torch.empty((geom.B, ns, HEAD_DIM), dtype=torch.float32, device=dev)
+    dgq = torch.empty((ns, HEAD_DIM), dtype=torch.float32, device=dev)
+    dgk = torch.empty((ns, HEAD_DIM), dtype=torch.float32, device=dev)
+    nbytes = bwd_workspace_bytes(geom)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().qi_joint_attn_bwd(geom.ptr(), _bshd(q_raw), _bshd(k_raw), _bshd(q), _bshd(k), _bshd(v), _bshd(o_f32),
+                                   _ptr(lse), _bshd(d_o), _ptr(gain_q), _ptr(gain_k), _bshd(dq), _bshd(dk),
+                                   _bshd(dv), _ptr(dgq_ps), _ptr(dgk_ps), _ptr(dgq), _ptr(dgk),
+                                   _ptr(workspace), workspace.numel(), _stream()))
+    return dict(dq=dq, dk=dk, dv=dv, dgain_q_ps=dgq_ps, dgain_k_ps=dgk_ps, dgain_q=dgq, dgain_k=dgk)
+
+
+def joint_attention(q_raw, k_raw, v, gain_q, gain_k, geom: Geometry, keep_f32=False):
+    """The whole forward path: prologue on Q and K, then attention.
+    Returns (q', k', O, LSE, O_f32) -- O_f32 (needed by the backward) only
+    when keep_f32, else None."""
+    q = qknorm_rope(q_raw, gain_q, geom)
+    k = qknorm_rope(k_raw, gain_k, geom)
+    of = torch.empty(q.shape, dtype=torch.float32, device=q.device) if keep_f32 else None
+    o, lse = joint_attn_fwd(q, k, v, geom, out_f32=of)
+    return q, k, o, lse, of
+
+
+def strict_probe(device: int = 0) -> None:
+    _check(lib().qi_strict_probe(int(device)))
+
+
+def trace() -> str:
+    return lib().qi_trace().decode()
+
+
+def last_error() -> str:
+    return lib().qi_last_error().decode()

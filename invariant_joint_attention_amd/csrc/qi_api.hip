@@ -1,0 +1,480 @@
+// qi_api.hip -- the C ABI declared in include/qi.h: argument validation, the
+// per-device gfx950 / strict-arithmetic gate, launch configuration and the
+// trace record.  No entry point allocates device memory.
+//
+// Pages: [Roadmap] "[RFC][Qwen-Image][CUDA/ROCm] WS1/WS2 kernel roadmap,
+// ablation matrix and integration plan", "Numerical requirements" (strict
+// configurations that are not supported fail closed) and "Work items"
+// (qwenimage_operator_trace); [Kernel list] "[RFC] [Qwen-Image] WS1
+// Single-GPU Kernel List", rules 4 and 7 (no fast math; trace records);
+// [PR 537] "[WS1][Qwen-Image][CUDA] AdaLN modulation projection
+// (adaln_mod_projection)": a probe kernel built with the library's own flags
+// checks the arithmetic, and its verdict is kept per device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/qi.h"
+#include "qi_common.h"
+#include "qi_kernels.h"
+
+using namespace qi;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+// ----------------------------------------------------------- validation
+struct Extent {
+  const char* name;
+  uintptr_t lo, hi;  // byte range [lo, hi)
+  bool output;
+};
+
+int check_geom(const qi_geom* g) {
+  if (!g) return fail(QI_E_INVALID, "geom is null");
+  if (g->D != kHeadDim) return fail(QI_E_UNSUPPORTED, "head dim %d unsupported (must be 128)", g->D);
+  if (g->B < 1 || g->H < 1) return fail(QI_E_INVALID, "B=%d H=%d must be >= 1", g->B, g->H);
+  if (g->T_txt < 0 || g->grid_h < 1 || g->grid_w < 1)
+    return fail(QI_E_INVALID, "T_txt=%d grid=%dx%d invalid", g->T_txt, g->grid_h, g->grid_w);
+  const int64_t S = (int64_t)g->T_txt + (int64_t)g->grid_h * g->grid_w;
+  if (S > (1 << 24)) return fail(QI_E_INVALID, "sequence length %lld too large", (long long)S);
+  if (g->rope_axes[0] != 16 || g->rope_axes[1] != 56 || g->rope_axes[2] != 56)
+    return fail(QI_E_UNSUPPORTED, "rope axes {%d,%d,%d} unsupported (must be {16,56,56})", g->rope_axes[0],
+                g->rope_axes[1], g->rope_axes[2]);
+  if (!(std::isfinite(g->rope_theta) && g->rope_theta > 1.0))
+    return fail(QI_E_INVALID, "rope_theta must be finite and > 1");
+  if (!(std::isfinite(g->rms_eps) && g->rms_eps > 0.f)) return fail(QI_E_INVALID, "rms_eps must be finite and > 0");
+  if (g->gain_streams != 1 && g->gain_streams != 2)
+    return fail(QI_E_INVALID, "gain_streams=%d must be 1 or 2", g->gain_streams);
+  if (!g->txt_len) return fail(QI_E_INVALID, "txt_len is null");
+  for (int b = 0; b < g->B; ++b)
+    if (g->txt_len[b] < 0 || g->txt_len[b] > g->T_txt)
+      return fail(QI_E_INVALID, "txt_len[%d]=%d outside [0, %d]", b, g->txt_len[b], g->T_txt);
+  return QI_OK;
+}
+
+int64_t seq_len(const qi_geom* g) { return (int64_t)g->T_txt + (int64_t)g->grid_h * g->grid_w; }
+
+// A [B,S,H,128] view: alignment, non-negative strides, and for outputs an
+// injective layout (no two elements share memory).
+int check_view(const qi_geom* g, const qi_bshd& v, int elsize, bool output, const char* name,
+               std::vector<Extent>& ext) {
+  if (!v.data) return fail(QI_E_INVALID, "%s is null", name);
+  if ((uintptr_t)v.data % 16) return fail(QI_E_ALIGN, "%s is not 16-byte aligned", name);
+  const int64_t S = seq_len(g);
+  const int64_t n[3] = {g->B, S, g->H};
+  const int64_t st[3] = {v.sb, v.ss, v.sh};
+  int64_t span = kHeadDim;  // elements reachable from the start
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] == 1) continue;
+    if (st[i] < 0) return fail(QI_E_INVALID, "%s has a negative stride", name);
+    if ((st[i] * elsize) % 16) return fail(QI_E_ALIGN, "%s stride %lld is not a multiple of 16 bytes", name,
+                                           (long long)st[i]);
+    span += (n[i] - 1) * st[i];
+  }
+  if (output) {
+    int idx[3] = {0, 1, 2};
+    std::sort(idx, idx + 3, [&](int x, int y) { return st[x] < st[y]; });
+    int64_t inner = kHeadDim;
+    for (int k = 0; k < 3; ++k) {
+      const int i = idx[k];
+      if (n[i] == 1) continue;
+      if (st[i] < inner) return fail(QI_E_ALIAS, "%s has overlapping elements (stride %lld)", name, (long long)st[i]);
+      inner = st[i] * n[i];
+    }
+  }
+  ext.push_back({name, (uintptr_t)v.data, (uintptr_t)v.data + (uintptr_t)(span * elsize), output});
+  return QI_OK;
+}
+
+int check_dense(const void* p, int64_t bytes, bool output, const char* name, std::vector<Extent>& ext,
+                bool nullable = false) {
+  if (!p) return nullable ? QI_OK : fail(QI_E_INVALID, "%s is null", name);
+  if ((uintptr_t)p % 16) return fail(QI_E_ALIGN, "%s is not 16-byte aligned", name);
+  ext.push_back({name, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, output});
+  return QI_OK;
+}
+
+int check_alias(const std::vector<Extent>& ext) {
+  for (size_t i = 0; i < ext.size(); ++i) {
+    if (!ext[i].output) continue;
+    for (size_t j = 0; j < ext.size(); ++j) {
+      if (i == j || (j < i && ext[j].output)) continue;
+      if (ext[i].lo < ext[j].hi && ext[j].lo < ext[i].hi)
+        return fail(QI_E_ALIAS, "output %s overlaps %s", ext[i].name, ext[j].name);
+    }
+  }
+  return QI_OK;
+}
+
+// ------------------------------------------------- device gate and probe
+__device__ uint32_t g_probe_out[8];
+
+__global__ void strict_probe_kernel(float sub, float three, float two, float tie1, float tie2, float zero,
+                                    float x, float y) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  g_probe_out[0] = __float_as_uint(sub * 1.5f);   // subnormal survives (no flush)
+  g_probe_out[1] = __float_as_uint(1.0f / three); // correctly rounded division
+  g_probe_out[2] = __float_as_uint(sqrtf(two));   // correctly rounded square root
+  g_probe_out[3] = pack_bf16x2(tie1, tie2);       // FP32 -> BF16 ties to even
+  g_probe_out[4] = __float_as_uint(__builtin_amdgcn_exp2f(zero));  // exp2(0) == 1 exactly
+  const float prod = x * x;                        // no contraction into an fma
+  g_probe_out[5] = __float_as_uint(prod - y);
+}
+
+uint32_t f2u(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
+std::mutex g_mu;
+std::map<int, int> g_dev_status;     // device id -> QI_OK / error code
+std::map<int, std::string> g_dev_msg;
+
+int run_probe(int dev) {
+  const float sub = std::ldexp(1.0f, -140), three = 3.0f, two = 2.0f;
+  const float tie1 = 1.0f + std::ldexp(1.0f, -8), tie2 = 1.0f + 3.0f * std::ldexp(1.0f, -8);
+  const float x = 1.0f + std::ldexp(1.0f, -12), y = 1.0f + std::ldexp(1.0f, -11);
+  hipLaunchKernelGGL(strict_probe_kernel, dim3(1), dim3(64), 0, 0, sub, three, two, tie1, tie2, 0.0f, x, y);
+  if (hipGetLastError() != hipSuccess) return fail(QI_E_HIP, "strict probe launch failed on device %d", dev);
+  uint32_t out[8] = {0};
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_probe_out), sizeof out, 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(QI_E_HIP, "strict probe readback failed on device %d", dev);
+  volatile float vthree = three, vtwo = two;
+  const uint32_t want[6] = {f2u(std::ldexp(3.0f, -141)), f2u(1.0f / vthree), f2u(std::sqrt(vtwo)),
+                            0x3F823F80u, f2u(1.0f), 0u};
+  const char* what[6] = {"subnormal multiply", "division rounding", "sqrt rounding", "bf16 RNE",
+                         "exp2(0)", "no fma contraction"};
+  for (int i = 0; i < 6; ++i)
+    if (out[i] != want[i])
+      return fail(QI_E_STRICT, "strict probe failed on device %d: %s (got 0x%08x want 0x%08x)", dev, what[i],
+                  out[i], want[i]);
+  return QI_OK;
+}
+
+int gate_device(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev_status.find(dev);
+  if (it != g_dev_status.end()) {
+    if (it->second != QI_OK) g_err = g_dev_msg[dev];
+    return it->second;
+  }
+  int st = QI_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    st = fail(QI_E_UNSUPPORTED, "cannot query HIP device %d", dev);
+  } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    st = fail(QI_E_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  } else {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != dev) (void)hipSetDevice(dev);
+    st = run_probe(dev);
+    if (cur != dev && cur >= 0) (void)hipSetDevice(cur);
+  }
+  g_dev_status[dev] = st;
+  g_dev_msg[dev] = st == QI_OK ? std::string() : g_err;
+  return st;
+}
+
+int current_device_gate() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(QI_E_UNSUPPORTED, "no HIP device available");
+  return gate_device(dev);
+}
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QI_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return QI_OK;
+}
+
+template <typename T>
+View<T> view_of(const qi_bshd& v, int64_t boff) {
+  return View<T>{(T*)v.data + boff * v.sb, v.sb, v.ss, v.sh};
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t dvec, pq, pk, total;
+  int n_txt_chunks, n_chunks;
+};
+
+BwdLayout bwd_layout(const qi_geom* g) {
+  BwdLayout L;
+  const int64_t S = seq_len(g);
+  L.n_txt_chunks = (int)ceil_div(g->T_txt, kPrologueChunk);
+  L.n_chunks = L.n_txt_chunks + (int)ceil_div((int64_t)g->grid_h * g->grid_w, kPrologueChunk);
+  L.dvec = 0;
+  L.pq = align256((size_t)g->B * g->H * S * 4);
+  const size_t part = align256((size_t)g->B * L.n_chunks * kHeadDim * 4);
+  L.pk = L.pq + part;
+  L.total = L.pk + part;
+  return L;
+}
+
+int launch_prologue(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd y, float* yf, hipStream_t st) {
+  PrologueArgs a;
+  a.x = view_of<const uint16_t>(x, 0);
+  a.y = view_of<uint16_t>(y, 0);
+  a.yf = yf;
+  a.gain = gain;
+  a.gain_streams = g->gain_streams;
+  a.B = g->B;
+  a.S = (int)seq_len(g);
+  a.H = g->H;
+  a.T_txt = g->T_txt;
+  a.gh = g->grid_h;
+  a.gw = g->grid_w;
+  a.theta = g->rope_theta;
+  a.eps = g->rms_eps;
+  const int64_t tokens = (int64_t)a.B * a.S;
+  hipLaunchKernelGGL(qknorm_rope_fwd_kernel, dim3((unsigned)ceil_div(tokens, 4)), dim3(256), 0, st, a);
+  return launched("qknorm_rope_fwd_kernel");
+}
+
+int launch_prologue_bwd(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd dx, float* partials,
+                        float* dg_ps, float* dg, const BwdLayout& Lw, hipStream_t st) {
+  PrologueBwdArgs a;
+  a.x = view_of<const uint16_t>(x, 0);
+  a.dx = view_of<float>(dx, 0);
+  a.gain = gain;
+  a.partials = partials;
+  a.gain_streams = g->gain_streams;
+  a.B = g->B;
+  a.S = (int)seq_len(g);
+  a.H = g->H;
+  a.T_txt = g->T_txt;
+  a.gh = g->grid_h;
+  a.gw = g->grid_w;
+  a.n_txt_chunks = Lw.n_txt_chunks;
+  a.n_chunks = Lw.n_chunks;
+  a.theta = g->rope_theta;
+  a.eps = g->rms_eps;
+  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(Lw.n_chunks, g->B), dim3(256), 0, st, a);
+  int rc = launched("qknorm_rope_bwd_kernel");
+  if (rc) return rc;
+  DgainFoldArgs f;
+  f.partials = partials;
+  f.dg_ps = dg_ps;
+  f.dg = dg;
+  f.B = g->B;
+  f.gain_streams = g->gain_streams;
+  f.n_txt_chunks = Lw.n_txt_chunks;
+  f.n_chunks = Lw.n_chunks;
+  hipLaunchKernelGGL(dgain_fold_kernel, dim3(g->gain_streams), dim3(kHeadDim), 0, st, f);
+  return launched("dgain_fold_kernel");
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+const char* qi_last_error(void) { return g_err.c_str(); }
+
+int qi_strict_probe(int device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n)
+    return fail(QI_E_UNSUPPORTED, "HIP device %d not available", device);
+  return gate_device(device);
+}
+
+int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y, float* y_f32,
+                   hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
+  if ((rc = check_view(geom, x, 2, false, "x", ext))) return rc;
+  if ((rc = check_dense(gain, (int64_t)geom->gain_streams * kHeadDim * 4, false, "gain", ext))) return rc;
+  if ((rc = check_view(geom, y, 2, true, "y", ext))) return rc;
+  if ((rc = check_dense(y_f32, n * 4, true, "y_f32", ext, true))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  return launch_prologue(geom, x, gain, y, y_f32, stream);
+}
+
+int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o, float* lse,
+                      float* o_f32, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+  if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
+  if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+
+  const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    FwdArgs a;
+    a.q = view_of<const uint16_t>(q, b0);
+    a.k = view_of<const uint16_t>(k, b0);
+    a.v = view_of<const uint16_t>(v, b0);
+    a.o = view_of<uint16_t>(o, b0);
+    a.lse = lse + (int64_t)b0 * geom->H * S;
+    a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
+    a.B = nb;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.n_qtiles = (int)ceil_div(S, rows_per_wg);
+    a.xcd_remap = ((nb * geom->H) % 8) == 0;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+    const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
+    if ((rc = launched("attn_fwd_kernel"))) return rc;
+  }
+  return QI_OK;
+}
+
+size_t qi_joint_attn_bwd_workspace(const qi_geom* geom) {
+  if (check_geom(geom)) return 0;
+  return bwd_layout(geom).total;
+}
+
+int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd q, qi_bshd k, qi_bshd v,
+                      qi_bshd o_f32, const float* lse, qi_bshd d_o, const float* gain_q, const float* gain_k,
+                      qi_bshd dq, qi_bshd dk, qi_bshd dv, float* dgain_q_ps, float* dgain_k_ps,
+                      float* dgain_q, float* dgain_k, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t gbytes = (int64_t)geom->gain_streams * kHeadDim * 4;
+  if ((rc = check_view(geom, q_raw, 2, false, "q_raw", ext))) return rc;
+  if ((rc = check_view(geom, k_raw, 2, false, "k_raw", ext))) return rc;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_view(geom, o_f32, 4, false, "o_f32", ext))) return rc;
+  if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, false, "lse", ext))) return rc;
+  if ((rc = check_view(geom, d_o, 2, false, "d_o", ext))) return rc;
+  if ((rc = check_dense(gain_q, gbytes, false, "gain_q", ext))) return rc;
+  if ((rc = check_dense(gain_k, gbytes, false, "gain_k", ext))) return rc;
+  if ((rc = check_view(geom, dq, 4, true, "dq", ext))) return rc;
+  if ((rc = check_view(geom, dk, 4, true, "dk", ext))) return rc;
+  if ((rc = check_view(geom, dv, 4, true, "dv", ext))) return rc;
+  if ((rc = check_dense(dgain_q_ps, geom->B * gbytes, true, "dgain_q_ps", ext))) return rc;
+  if ((rc = check_dense(dgain_k_ps, geom->B * gbytes, true, "dgain_k_ps", ext))) return rc;
+  if ((rc = check_dense(dgain_q, gbytes, true, "dgain_q", ext, true))) return rc;
+  if ((rc = check_dense(dgain_k, gbytes, true, "dgain_k", ext, true))) return rc;
+  const BwdLayout Lw = bwd_layout(geom);
+  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < Lw.total)
+    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, Lw.total);
+  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + Lw.total, true});
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+
+  char* ws = (char*)workspace;
+  float* Dvec = (float*)(ws + Lw.dvec);
+  const int rows_per_wg = 128;
+  int nk_max = 0;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    BwdArgs a;
+    a.q = view_of<const uint16_t>(q, b0);
+    a.k = view_of<const uint16_t>(k, b0);
+    a.v = view_of<const uint16_t>(v, b0);
+    a.o = view_of<const float>(o_f32, b0);
+    a.dO = view_of<const uint16_t>(d_o, b0);
+    a.lse = lse + (int64_t)b0 * geom->H * S;
+    a.Dvec = Dvec + (int64_t)b0 * geom->H * S;
+    a.dq = view_of<float>(dq, b0);
+    a.dk = view_of<float>(dk, b0);
+    a.dv = view_of<float>(dv, b0);
+    a.B = nb;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.n_qtiles = (int)ceil_div(S, rows_per_wg);
+    nk_max = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int L = geom->txt_len[b0 + i];
+      const int nk = (int)(ceil_div(L, 128) + ceil_div(a.T_img, 128) + ceil_div(geom->T_txt - L, 128));
+      nk_max = std::max(nk_max, nk);
+    }
+    a.n_ktiles = nk_max;
+    a.xcd_remap = ((nb * geom->H) % 8) == 0;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(256), 0,
+                       stream, a);
+    if ((rc = launched("attn_bwd_dq_kernel"))) return rc;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_ktiles)), dim3(256), 0,
+                       stream, a);
+    if ((rc = launched("attn_bwd_dkdv_kernel"))) return rc;
+  }
+  if ((rc = launch_prologue_bwd(geom, q_raw, gain_q, dq, (float*)(ws + Lw.pq), dgain_q_ps, dgain_q, Lw, stream)))
+    return rc;
+  return launch_prologue_bwd(geom, k_raw, gain_k, dk, (float*)(ws + Lw.pk), dgain_k_ps, dgain_k, Lw, stream);
+}
+
+const char* qi_trace(void) {
+  static const std::string s = [] {
+    char buf[4096];
+    snprintf(buf, sizeof buf,
+             "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":1,"
+             "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dkdv\":\"attn_bwd_dkdv_kernel\"},"
+             "\"mfma\":\"v_mfma_f32_32x32x16_bf16\",\"accumulator\":\"fp32\","
+             "\"frozen\":{\"fwd_key_tile\":%d,\"bwd_dq_key_tile\":%d,\"bwd_dkdv_query_tile\":%d,"
+             "\"prologue_dgain_chunk\":%d,\"key_order\":\"text tiles from 0, image tiles from T_txt\","
+             "\"bwd_query_order\":\"valid text, image, padded text\","
+             "\"softmax\":\"exp2(fma(s,log2e/sqrt(128),-m*c)); l sums fp32 P in register order\","
+             "\"fwd_p_split\":\"hi=bf16(P), lo=bf16(P-hi), accumulated hi then lo\","
+             "\"bwd_D\":\"rowsum(dO*O) from the fp32 forward O\","
+             "\"reference_max_threshold_log2\":8,"
+             "\"ds_split\":\"hi=bf16(dS), lo=bf16(dS-hi), accumulated hi then lo (dQ, dK)\","
+             "\"dv_p_split\":\"hi=bf16(P), lo=bf16(P-hi), accumulated hi then lo\","
+             "\"rms_sum_tree\":\"8 sequential per lane, xor 8,4,2,1\","
+             "\"dgain_fold\":\"chunks ascending per sample, then samples ascending\"},"
+             "\"free\":[\"rows per workgroup\",\"grid order / XCD mapping\",\"LDS layout\",\"prefetch depth\"],"
+             "\"split_k\":false,\"split_kv\":false,\"stream_k\":false,\"atomics\":false,\"tf32\":false,"
+             "\"fast_math\":false,\"fp_contract\":\"off\",\"fp32_denormals\":\"preserved\","
+             "\"div_sqrt\":\"correctly rounded\",\"exp2\":\"v_exp_f32\","
+             "\"rope_angles\":\"fp64, cos/sin rounded once to fp32\",\"output_cast\":\"fp32->bf16 RNE, once\","
+             "\"hipcc\":\"%s\"}",
+             kFwdBN, kBwdBN, kBwdBM, kPrologueChunk, __clang_version__);
+    return std::string(buf);
+  }();
+  return s.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// qi_kernels.h -- kernel argument blocks and kernel declarations.
+#pragma once
+
+#include "qi_common.h"
+
+namespace qi {
+
+constexpr int kPrologueChunk = 16;  // tokens per gain-gradient partial (frozen)
+
+struct PrologueArgs {
+  View<const uint16_t> x;
+  View<uint16_t> y;
+  float* yf;  // nullable dense [B,S,H,128]
+  const float* gain;
+  int gain_streams;
+  int B, S, H, T_txt, gh, gw;
+  double theta;
+  float eps;
+};
+
+struct PrologueBwdArgs {
+  View<const uint16_t> x;  // raw BF16 input of the prologue
+  View<float> dx;          // in: dL/dy (pre-rotation gradient); out: dL/dx
+  const float* gain;
+  float* partials;  // [B][n_chunks][128]
+  int gain_streams;
+  int B, S, H, T_txt, gh, gw;
+  int n_txt_chunks, n_chunks;
+  double theta;
+  float eps;
+};
+
+struct DgainFoldArgs {
+  const float* partials;  // [B][n_chunks][128]
+  float* dg_ps;           // [B][gain_streams][128]
+  float* dg;              // nullable [gain_streams][128]
+  int B, gain_streams, n_txt_chunks, n_chunks;
+};
+
+// Forward attention.  One launch covers up to kMaxBatchPerLaunch rows.
+constexpr int kFwdBN = 64;        // key tile width (frozen: part of the arithmetic contract)
+constexpr int kFwdWaves = 4;      // waves per workgroup (free)
+constexpr int kFwdRowsPerWave = 32;
+
+struct FwdArgs {
+  View<const uint16_t> q, k, v;
+  View<uint16_t> o;
+  float* lse;  // dense [B,H,S] (B of this launch)
+  float* of;   // nullable dense [B,S,H,128]
+  int B, S, H, T_txt, T_img;
+  int n_qtiles;   // ceil(S / rows per workgroup)
+  int xcd_remap;  // 1: group the query tiles of a (b, h) on one XCD
+  int txt_len[kMaxBatchPerLaunch];
+};
+
+// Backward attention.
+constexpr int kBwdBN = 64;  // key tile of the dQ pass (= forward order)
+constexpr int kBwdBM = 64;  // query tile of the dK/dV pass (frozen)
+
+struct BwdArgs {
+  View<const uint16_t> q, k, v, dO;
+  View<const float> o;  // FP32 pre-cast forward output
+  const float* lse;  // [B,H,S]
+  float* Dvec;       // [B,H,S] workspace: rowsum(dO * O)
+  View<float> dq, dk, dv;
+  int B, S, H, T_txt, T_img;
+  int n_qtiles, n_ktiles;
+  int xcd_remap;
+  int txt_len[kMaxBatchPerLaunch];
+};
+
+__global__ void qknorm_rope_fwd_kernel(PrologueArgs a);
+__global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
+__global__ void dgain_fold_kernel(DgainFoldArgs a);
+__global__ void attn_fwd_kernel(FwdArgs a);
+__global__ void attn_bwd_dq_kernel(BwdArgs a);
+__global__ void attn_bwd_dkdv_kernel(BwdArgs a);
+
+}  // namespace qi

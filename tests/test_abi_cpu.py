@@ -1,0 +1,161 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+that include/qi.h declares, rejects invalid arguments before touching a device
+(no compute is launched here: there is no GPU), and reports its contract."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import invariant_joint_attention_amd as qi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qi.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qi.LIB_PATH), reason="libqi.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_lists_the_binding_symbols():
+    assert declared_symbols() == sorted(qi.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qi.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (qi_\w+)", out))
+    assert set(declared_symbols()) <= exported
+
+
+def test_trace_is_json_with_the_frozen_contract():
+    t = json.loads(qi.trace())
+    assert t["target"] == "gfx950"
+    assert t["split_k"] is False and t["split_kv"] is False and t["atomics"] is False
+    assert t["fast_math"] is False and t["fp_contract"] == "off"
+    assert t["frozen"]["fwd_key_tile"] == 64
+
+
+# Fake, never-dereferenced device addresses (validation only looks at them).
+BASE = 0x7F0000000000
+
+
+def fake_bshd(addr, B, S, H, sb=None, ss=None, sh=None):
+    sh = 128 if sh is None else sh
+    ss = H * sh if ss is None else ss
+    sb = S * ss if sb is None else sb
+    return qi.QiBshd(addr, sb, ss, sh)
+
+
+def region(i):
+    return BASE + i * (1 << 32)
+
+
+def fwd_call(geom, q=None, k=None, v=None, o=None, lse=None, of=None):
+    g = geom
+    q = q or fake_bshd(region(0), g.B, g.S, g.H)
+    k = k or fake_bshd(region(1), g.B, g.S, g.H)
+    v = v or fake_bshd(region(2), g.B, g.S, g.H)
+    o = o or fake_bshd(region(3), g.B, g.S, g.H)
+    lse = region(4) if lse is None else lse
+    return qi.lib().qi_joint_attn_fwd(g.ptr(), q, k, v, o, lse, of, None)
+
+
+def geom(**kw):
+    args = dict(B=1, H=2, T_txt=8, grid_h=4, grid_w=4, txt_len=[5])
+    args.update(kw)
+    return qi.Geometry(**args)
+
+
+def code(name):
+    return {v: k for k, v in qi.STATUS.items()}[name]
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=64), "QI_E_UNSUPPORTED"),
+    (dict(rope_axes=(16, 48, 64)), "QI_E_UNSUPPORTED"),
+    (dict(B=0, txt_len=[]), "QI_E_INVALID"),
+    (dict(H=0), "QI_E_INVALID"),
+    (dict(grid_h=0), "QI_E_INVALID"),
+    (dict(T_txt=-1), "QI_E_INVALID"),
+    (dict(txt_len=[9]), "QI_E_INVALID"),
+    (dict(txt_len=[-1]), "QI_E_INVALID"),
+    (dict(rms_eps=0.0), "QI_E_INVALID"),
+    (dict(rms_eps=float("nan")), "QI_E_INVALID"),
+    (dict(rope_theta=float("inf")), "QI_E_INVALID"),
+    (dict(gain_streams=3), "QI_E_INVALID"),
+])
+def test_invalid_geometry_fails_closed(kw, expect):
+    g = geom(**kw)
+    assert fwd_call(g) == code(expect)
+    assert qi.last_error() != ""
+    assert qi.lib().qi_joint_attn_bwd_workspace(g.ptr()) == 0
+
+
+def test_null_and_misaligned_pointers():
+    g = geom()
+    assert fwd_call(g, q=qi.QiBshd(0, 0, 0, 0)) == code("QI_E_INVALID")
+    assert fwd_call(g, q=fake_bshd(region(0) + 8, g.B, g.S, g.H)) == code("QI_E_ALIGN")
+    assert fwd_call(g, lse=region(4) + 4) == code("QI_E_ALIGN")
+    # a stride that is not a multiple of 16 bytes
+    assert fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, sh=132)) == code("QI_E_ALIGN")
+    assert fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, sh=-128)) == code("QI_E_INVALID")
+
+
+def test_aliasing_is_rejected():
+    g = geom()
+    # output equal to an input
+    assert fwd_call(g, o=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    # output overlapping the LSE buffer
+    assert fwd_call(g, lse=region(3) + 256) == code("QI_E_ALIAS")
+    # an output view whose elements overlap each other (head stride 64 < 128)
+    assert fwd_call(g, o=fake_bshd(region(3), g.B, g.S, g.H, sh=64)) == code("QI_E_ALIAS")
+    # inputs may alias each other (q = k) -- only outputs are exclusive
+    rc = fwd_call(g, k=fake_bshd(region(0), g.B, g.S, g.H))
+    assert rc != code("QI_E_ALIAS")
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    """All arguments valid: the only failure left on a GPU-less host is the
+    device gate, and nothing is launched."""
+    g = geom()
+    rc = fwd_call(g)
+    assert rc == code("QI_E_UNSUPPORTED"), qi.last_error()
+
+
+def test_prologue_and_backward_validation():
+    g = geom()
+    L = qi.lib()
+    x = fake_bshd(region(0), g.B, g.S, g.H)
+    y = fake_bshd(region(1), g.B, g.S, g.H)
+    assert L.qi_qknorm_rope(g.ptr(), x, region(2), x, None, None) == code("QI_E_ALIAS")
+    assert L.qi_qknorm_rope(g.ptr(), x, None, y, None, None) == code("QI_E_INVALID")
+    assert L.qi_qknorm_rope(g.ptr(), x, region(2), y, region(3) + 4, None) == code("QI_E_ALIGN")
+    ws = L.qi_joint_attn_bwd_workspace(g.ptr())
+    assert ws > 0 and ws % 256 == 0
+    views = [fake_bshd(region(i), g.B, g.S, g.H) for i in range(6)]
+    dout = fake_bshd(region(7), g.B, g.S, g.H)
+    grads = [fake_bshd(region(10 + i), g.B, g.S, g.H, sh=128) for i in range(3)]
+
+    def bwd(ws_ptr=region(20), ws_bytes=ws, dq=None):
+        return L.qi_joint_attn_bwd(g.ptr(), *views, region(6), dout, region(8), region(9),
+                                   dq or grads[0], grads[1], grads[2], region(14), region(15), None, None,
+                                   ws_ptr, ws_bytes, None)
+
+    assert bwd(ws_ptr=None) == code("QI_E_WORKSPACE")
+    assert bwd(ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    assert bwd(ws_ptr=region(20) + 16) == code("QI_E_ALIGN")
+    assert bwd(dq=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    assert bwd() == code("QI_E_UNSUPPORTED")
+
+
+def test_strict_probe_without_gpu():
+    assert qi.lib().qi_strict_probe(0) == code("QI_E_UNSUPPORTED")

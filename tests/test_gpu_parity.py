@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes are compared element by element over every output; the full
+reference shapes are compared on sampled (batch, head, row-range) slices the
+oracle computes one by one, in the same launch configuration bench.py times.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import Oracle, fold_batch
+from parity import abs_check, f64, mixed_check
+
+qi = pytest.importorskip("invariant_joint_attention_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return Oracle("f32")
+
+
+def gpu_inputs(wl, **kw):
+    inp = workloads.make_inputs(wl, **kw)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    return inp, g
+
+
+def geom_of(wl, txt_len=None, gain_streams=1, B=None):
+    return qi.Geometry(B=wl.B if B is None else B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w,
+                       txt_len=list(wl.txt_len if txt_len is None else txt_len), gain_streams=gain_streams)
+
+
+SMALL = [  # name, B, H, T_txt, txt_len, h, w
+    ("tiny", 1, 2, 8, (5,), 4, 4),
+    ("ragged_odd", 2, 3, 7, (0, 7), 5, 3),
+    ("one_image_token", 2, 1, 3, (0, 2), 1, 1),
+    ("no_text", 1, 2, 0, (0,), 6, 5),
+    ("multi_tile", 2, 2, 100, (77, 3), 13, 11),
+    ("wide", 1, 3, 70, (64,), 9, 20),
+]
+
+
+def small_wl(spec, seed=100, backward=False):
+    name, B, H, T, Ls, h, w = spec
+    return workloads.custom(name, B, H, T, Ls, h, w, seed, backward=backward)
+
+
+def test_strict_probe():
+    qi.strict_probe(0)
+
+
+def test_trace_mentions_mfma():
+    assert "v_mfma_f32_32x32x16_bf16" in qi.trace()
+
+
+# ------------------------------------------------------------------ prologue
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("streams", [1, 2])
+def test_prologue_small(orc, spec, streams):
+    wl = small_wl(spec)
+    inp, g = gpu_inputs(wl, gain_streams=streams)
+    geo = geom_of(wl, gain_streams=streams)
+    for name, gain in (("q", "g_q"), ("k", "g_k")):
+        yf = torch.empty(g[name].shape, dtype=torch.float32, device=DEV)
+        y = qi.qknorm_rope(g[name], g[gain], geo, out_f32=yf)
+        torch.cuda.synchronize()
+        ref = orc.qknorm_rope(orc.widen(workloads.bits(inp[name])), inp[gain].numpy(), wl.T_txt, wl.h, wl.w)
+        abs_check(yf, ref, f"{name}' fp32")
+        mixed_check(y, ref, f"{name}' bf16")
+        # the BF16 output is the single RNE cast of the FP32 value
+        assert torch.equal(y.cpu(), yf.cpu().to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("cfg", ["1024sq", "1328sq_cfg", "1664x928"])
+def test_prologue_full(orc, cfg):
+    wl = workloads.WORKLOADS[cfg]
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    yf = torch.empty(g["q"].shape, dtype=torch.float32, device=DEV)
+    y = qi.qknorm_rope(g["q"], g["g_q"], geo, out_f32=yf)
+    torch.cuda.synchronize()
+    ref = orc.qknorm_rope(orc.widen(workloads.bits(inp["q"])), inp["g_q"].numpy(), wl.T_txt, wl.h, wl.w)
+    abs_check(yf, ref, "q' fp32")
+    mixed_check(y, ref, "q' bf16")
+
+
+# ------------------------------------------------------------------- forward
+def _fwd_all(g, geo, with_f32=False):
+    q = qi.qknorm_rope(g["q"], g["g_q"], geo)
+    k = qi.qknorm_rope(g["k"], g["g_k"], geo)
+    of = torch.empty(q.shape, dtype=torch.float32, device=DEV) if with_f32 else None
+    o, lse = qi.joint_attn_fwd(q, k, g["v"], geo, out_f32=of)
+    torch.cuda.synchronize()
+    return q, k, o, lse, of
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+def test_forward_small(orc, spec):
+    wl = small_wl(spec)
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    q, k, o, lse, of = _fwd_all(g, geo, with_f32=True)
+    # isolation: the oracle attends over the GPU's own q', k'
+    ro, rl = orc.attn_fwd(f64(q), f64(k), f64(inp["v"].float()), wl.txt_len, wl.T_txt)
+    mixed_check(o, ro, "O bf16")
+    mixed_check(of, ro, "O fp32")
+    abs_check(lse, rl, "LSE")
+    # end to end from the raw inputs
+    from oracle import forward_path
+    fw = forward_path(orc, workloads.bits(inp["q"]), workloads.bits(inp["k"]), workloads.bits(inp["v"]),
+                      inp["g_q"].numpy(), inp["g_k"].numpy(), wl.txt_len, wl.T_txt, wl.h, wl.w)
+    mixed_check(o, fw["o"], "O end-to-end")
+    abs_check(lse, fw["lse"], "LSE end-to-end", atol=2e-3)
+
+
+def _sample_rows(wl):
+    S, T = wl.S, wl.T_txt
+    rngs = [(0, min(32, S)), (max(0, T - 16), min(S, T + 48)), (max(0, S - 40), S)]
+    return rngs
+
+
+@pytest.mark.parametrize("cfg", ["1024sq", "1328sq_cfg", "1664x928"])
+def test_forward_full_sampled(orc, cfg):
+    wl = workloads.WORKLOADS[cfg]
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    q, k, o, lse, _ = _fwd_all(g, geo)
+    qn, kn, on, ln = f64(q), f64(k), f64(o), f64(lse)
+    vn = f64(inp["v"].float())
+    heads = [0, wl.H // 2, wl.H - 1]
+    for b in range(wl.B):
+        for h in heads:
+            for s0, s1 in _sample_rows(wl):
+                ro, rl = orc.attn_fwd_bh(qn[b, :, h], kn[b, :, h], vn[b, :, h], wl.T_txt, wl.txt_len[b], s0, s1)
+                mixed_check(on[b, s0:s1, h], ro, f"O b{b} h{h} rows {s0}:{s1}")
+                abs_check(ln[b, h, s0:s1], rl, f"LSE b{b} h{h} rows {s0}:{s1}")
+
+
+def test_forward_constant_v_and_scaling():
+    wl = small_wl(("c", 1, 2, 40, (29,), 9, 7), seed=5)
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    q = qi.qknorm_rope(g["q"], g["g_q"], geo)
+    k = qi.qknorm_rope(g["k"], g["g_k"], geo)
+    vc = g["v"][:, :1].expand_as(g["v"]).contiguous()
+    oc, _ = qi.joint_attn_fwd(q, k, vc, geo)
+    assert torch.equal(oc, vc), "constant V must be returned exactly"
+    o1, l1 = qi.joint_attn_fwd(q, k, g["v"], geo)
+    o2, l2 = qi.joint_attn_fwd(q, k, (g["v"].float() * 2).to(torch.bfloat16), geo)
+    assert torch.equal(o2, (o1.float() * 2).to(torch.bfloat16)) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_all(g, geo):
+    q, k, o, lse, of = _fwd_all(g, geo, with_f32=True)
+    r = qi.joint_attn_bwd(g["q"], g["k"], q, k, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo)
+    torch.cuda.synchronize()
+    return q, k, o, lse, r
+
+
+BWD_SMALL = [s for s in SMALL if s[0] != "wide"] + [("wide", 1, 3, 70, (64,), 9, 20)]
+
+
+@pytest.mark.parametrize("spec", BWD_SMALL, ids=[s[0] for s in BWD_SMALL])
+@pytest.mark.parametrize("streams", [1, 2])
+def test_backward_small(orc, spec, streams):
+    wl = small_wl(spec, backward=True)
+    inp, g = gpu_inputs(wl, gain_streams=streams)
+    geo = geom_of(wl, gain_streams=streams)
+    q, k, o, lse, r = _bwd_all(g, geo)
+    # oracle: attention gradients at the GPU's q', k' (isolation), then the
+    # prologue backward from the raw inputs
+    dqp, dkp, dv = orc.attn_bwd(f64(q), f64(k), f64(inp["v"].float()), f64(inp["dO"].float()), wl.txt_len, wl.T_txt)
+    dq, dgq = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["q"])), inp["g_q"].numpy(), dqp, wl.T_txt, wl.h, wl.w)
+    dk, dgk = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["k"])), inp["g_k"].numpy(), dkp, wl.T_txt, wl.h, wl.w)
+    mixed_check(r["dv"], dv, "dv")
+    mixed_check(r["dq"], dq, "dq")
+    mixed_check(r["dk"], dk, "dk")
+    mixed_check(r["dgain_q_ps"], dgq, "dgain_q per sample")
+    mixed_check(r["dgain_k_ps"], dgk, "dgain_k per sample")
+    mixed_check(r["dgain_q"], fold_batch(dgq), "dgain_q")
+    mixed_check(r["dgain_k"], fold_batch(dgk), "dgain_k")
+    # masked keys receive exactly zero
+    for b in range(wl.B):
+        L = wl.txt_len[b]
+        assert not r["dv"][b, L:wl.T_txt].any() and not r["dk"][b, L:wl.T_txt].any()
+
+
+def test_backward_full_sampled_head(orc):
+    wl = workloads.WORKLOADS["1024sq_bwd"]
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    q, k, o, lse, r = _bwd_all(g, geo)
+    h = 5
+    b = 0
+    qn, kn = f64(q)[b:b + 1, :, h:h + 1], f64(k)[b:b + 1, :, h:h + 1]
+    vn, dn = f64(inp["v"].float())[b:b + 1, :, h:h + 1], f64(inp["dO"].float())[b:b + 1, :, h:h + 1]
+    dqp, dkp, dv = orc.attn_bwd(qn, kn, vn, dn, wl.txt_len, wl.T_txt)
+    xq = orc.widen(workloads.bits(inp["q"]))[b:b + 1, :, h:h + 1]
+    xk = orc.widen(workloads.bits(inp["k"]))[b:b + 1, :, h:h + 1]
+    dq, _ = orc.qknorm_rope_bwd(xq, inp["g_q"].numpy(), dqp, wl.T_txt, wl.h, wl.w)
+    dk, _ = orc.qknorm_rope_bwd(xk, inp["g_k"].numpy(), dkp, wl.T_txt, wl.h, wl.w)
+    mixed_check(r["dv"][b:b + 1, :, h:h + 1], dv, "dv head 5")
+    mixed_check(r["dq"][b:b + 1, :, h:h + 1], dq, "dq head 5")
+    mixed_check(r["dk"][b:b + 1, :, h:h + 1], dk, "dk head 5")
