@@ -123,6 +123,9 @@ int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
  * P enters the A.V product as two BF16 terms (hi = bf16(p), lo = bf16(p-hi))
  * so the output meets 1e-2*|ref| + 2e-3 even where O cancels on a few
  * peaked keys; the row sum uses the FP32 p.
+ * The sequence stride of k and v must stay below 2^26 elements (the kernel
+ * addresses 16 key rows from one base with 32-bit offsets); larger strides
+ * return QI_E_UNSUPPORTED.
  */
 int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o,
                       float* lse, float* o_f32, hipStream_t stream);

@@ -335,6 +335,8 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   if ((rc = check_alias(ext))) return rc;
   if ((rc = current_device_gate())) return rc;
 
+  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride))
+    return fail(QI_E_UNSUPPORTED, "k/v sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);

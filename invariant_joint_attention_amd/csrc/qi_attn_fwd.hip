@@ -7,26 +7,26 @@
 // rows Streams and Text input, and "Numerical requirements" (fixed reduction
 // trees, FP32 accumulation, no split-KV, one output cast, batch invariance).
 //
-// Design (per workgroup: 4 waves x 32 query rows of one (b, h)):
+// Arithmetic (frozen; every launch shape gives the same bits):
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    A = a 32-key block of K read from LDS, B = the wave's Q rows, kept in
-//    registers for the whole key loop.  Lane l then owns query l%32 and 16
-//    keys per block, so the row max is an in-lane max plus one exchange with
-//    lane l^32, and the softmax rescale factor is a per-lane scalar.
-//  * O^T = V^T P^T accumulates in 4 blocks of 32x32 FP32 (64 registers).  P
-//    is taken straight from the score accumulators and enters the MFMA as two
-//    BF16 terms, hi = bf16(p) and lo = bf16(p - hi), accumulated hi then lo:
-//    one BF16 rounding of P alone would move O by up to 2^-9 * sum_j p_j|v_j|,
-//    which breaks the output tolerance where O cancels on few, peaked keys.
-//    The MFMA reduction index is a permutation of the 16 keys of a chunk
-//    (bits 2 and 3 of the key index swapped) that matches the accumulator
-//    layout of P; the transposing V reads fetch the keys in that order.
+//    A = a 32-key block of K, B = 32 query rows of Q held in registers for
+//    the whole key loop.  Lane l owns query l%32 and 16 keys per block, so
+//    the row max is an in-lane max plus one exchange with lane l^32, and the
+//    softmax rescale factor is a per-lane scalar.  Each 32-key block
+//    accumulates its 8 head-dim chunks in order.
+//  * O^T = V^T P^T accumulates in 4 blocks of 32x32 FP32.  P enters the MFMA
+//    as two BF16 terms, hi = bf16(p) and lo = bf16(p - hi), accumulated hi
+//    then lo for each 16-key chunk in key order: one BF16 rounding of P
+//    alone would move O by up to 2^-9 * sum_j p_j|v_j|, which breaks the
+//    output tolerance where O cancels on few, peaked keys.  The MFMA
+//    reduction index is a permutation of the 16 keys of a chunk (bits 2 and
+//    3 of the key index swapped) that matches the accumulator layout of P;
+//    the transposing V reads fetch the keys in that order.
 //  * Keys are tiled LOGICALLY: ceil(L_b/64) text tiles starting at key 0,
 //    then ceil(T_img/64) image tiles starting at key T_txt.  Masked keys are
 //    never read (their LDS slots are zero) and get probability exactly 0, so
 //    a row's arithmetic does not depend on T_txt, on the batch or on the
-//    workgroup shape.  The key tile width 64 is frozen; rows per workgroup,
-//    grid order and LDS layout are free.
+//    workgroup shape.  The key tile width 64 is frozen.
 //  * Online softmax in the exp2 domain with c = log2(e)/sqrt(128):
 //    p = exp2(s*c - m*c) (one fma); the row sum l adds the FP32 p lane by lane
 //    in register order, then the two half-waves (commutative, so both get the
@@ -35,18 +35,31 @@
 //    8/c (so p <= 256): each lane decides from its own row alone, and the
 //    rescale (factor exactly 1 where m did not move) is skipped when no lane
 //    of the wave moved.
-//  * K/V tiles are double-buffered in LDS and filled by direct global->LDS
-//    loads (global_load_lds_dwordx4, no registers), issued for tile t+1
-//    while tile t is multiplied.  Rows are unpadded 256-byte lines whose
-//    16-byte chunks are XOR-swizzled by key, so the K fragment reads, the V
-//    transposing reads and the loads' contiguous LDS writes avoid bank
-//    conflicts.  V stays row-major: ds_read_b64_tr_b16 delivers the
-//    transposed V^T fragment of the A*V product straight from LDS.
-//  * Two waves per SIMD (at most 256 VGPRs), 4 waves x 32 rows per
-//    workgroup; s_setprio raises the MFMA sections' priority so one wave's
-//    softmax overlaps the other wave's matrix work.
+//
+// Schedule (free; does not change any bit):
+//  * Workgroup = 8 waves x 32 query rows of one (b, h).  Waves w and w+4 run
+//    on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) alternate
+//    between a matrix phase (P*V of tile t plus the scores of tile t+1, 48
+//    MFMAs) and a softmax phase (VALU only), one workgroup barrier per phase,
+//    so each SIMD has one wave issuing MFMAs while its partner runs the
+//    softmax.  Group 1 starts one barrier later; both run 2*nt + 1 barriers.
+//  * LDS: K tiles in kbuf[j & 1], V tiles in vbuf[j & 1], 64 KiB.  Rows are
+//    unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key, so
+//    the K fragment reads, the transposing V reads (ds_read_b64_tr_b16, V
+//    stays row-major) and the contiguous direct-load writes avoid bank
+//    conflicts.  Group 1 fills the tiles with direct global->LDS loads
+//    (global_load_lds_dwordx4) in its softmax phase of tile t: K_{t+2} and
+//    V_{t+1}, whose buffers were last read in the matrix phases of tile
+//    t-1; it waits for them (vmcnt) at the end of its matrix phase of tile
+//    t, one barrier before group 0 reads them.
+//  * The matrix phase issues its LDS reads as inline asm two steps ahead of
+//    use and waits for each step's reads with an exact lgkmcnt; the direct
+//    loads are inline asm too, so the compiler neither inserts waits for
+//    them before unrelated LDS reads nor keeps 64-bit addresses for them.
 #include "qi_common.h"
 #include "qi_kernels.h"
+
+#include <type_traits>
 
 namespace qi {
 
@@ -54,7 +67,6 @@ namespace {
 
 constexpr int kRowB = 256;                   // bytes per K / V row in LDS (unpadded, chunk-swizzled)
 constexpr int kTileB = kFwdBN * kRowB;       // 16384
-constexpr int kBufBytes = 2 * kTileB;        // K tile then V tile
 // log2(e) / sqrt(128), rounded once to FP32
 constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -87,58 +99,285 @@ __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, i
   }
 }
 
-// Global -> LDS without registers (global_load_lds_dwordx4): wave w fills
-// keys 16w..16w+15 of the K and V tiles, 4 keys (1 KiB) per instruction;
-// lane l writes LDS slot l of the instruction's block, i.e. physical chunk
-// l%16 of key 4i + l/16, so it fetches the logical chunk that the swizzle
-// maps there.  Keys past the tile's valid count are not read; their slots
-// are zero-filled so a masked key never contributes a NaN to P*V.
-__device__ __forceinline__ void load_tile_async(const FwdArgs& a, char* buf, int b, int h, int key0,
-                                                int nvalid, int wave, int lane) {
+// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4
+// with a scalar base and a 32-bit lane offset): lane l's bytes land at LDS
+// byte lds + 16*l.  Issued as inline asm, so the compiler neither waits for
+// it before unrelated LDS reads nor spills 64-bit addresses for it; the
+// kernel waits for these loads explicitly (vmcnt) before the barrier that
+// publishes the tile.  M0 (the LDS destination) is written here and has no
+// other user in this kernel: no LDS-DMA builtin, GWS or message send, so the
+// compiler keeps nothing in it that the clobber could destroy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Global -> LDS tile fill: wave `sub` of a group fills keys 16*sub..16*sub+15
+// of one 64-key tile, 4 keys (1 KiB) per instruction; lane l writes LDS slot
+// l of the instruction's block, i.e. physical chunk l%16 of key 4i + l/16,
+// so it fetches the logical chunk that the swizzle maps there.  Keys past
+// the tile's valid count are not read; their slots are zero-filled so a
+// masked key never contributes a NaN.
+struct RowOff {
+  uint32_t o[4];
+};
+__device__ __forceinline__ RowOff row_offsets(int64_t ss, int lane) {
+  RowOff r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int kt = 16 * wave + 4 * i;           // first key of this 1 KiB block
-    const int key = kt + (lane >> 4);
-    const int chunk = (lane & 15) ^ swz(key);   // logical chunk stored in slot lane
-    lds_char* kdst = (lds_char*)(buf + kt * kRowB);
-    lds_char* vdst = (lds_char*)(buf + kTileB + kt * kRowB);
-    if (key < nvalid) {
-      __builtin_amdgcn_global_load_lds((const void*)(a.k.row(b, key0 + key, h) + 8 * chunk), (void __attribute__((address_space(3)))*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(a.v.row(b, key0 + key, h) + 8 * chunk), (void __attribute__((address_space(3)))*)vdst, 16, 0, 0);
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4*)(buf + kt * kRowB + 16 * lane) = z;
-      *(u32x4*)(buf + kTileB + kt * kRowB + 16 * lane) = z;
+    const int kl = 4 * i + (lane >> 4);       // key within a wave's 16
+    const int chunk = (lane & 15) ^ swz(kl);  // swz depends on key % 16 only
+    r.o[i] = (uint32_t)(kl * (uint32_t)ss + 8 * chunk) * 2u;
+  }
+  return r;
+}
+__device__ __forceinline__ void load_rows(const View<const uint16_t>& src, const RowOff& ro, char* dst, int b,
+                                          int h, int key0, int nvalid, int sub, int lane) {
+  const char* base = (const char*)(src.p + (int64_t)b * src.sb + (int64_t)h * src.sh +
+                                   (int64_t)(key0 + 16 * sub) * src.ss);
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(dst + 16 * sub * kRowB);
+  if (nvalid >= 16 * sub + 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(base, ro.o[i], lds + 4 * i * kRowB);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (16 * sub + 4 * i + (lane >> 4) < nvalid) {
+        dma16(base, ro.o[i], lds + 4 * i * kRowB);
+      } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *(u32x4*)(dst + (16 * sub + 4 * i) * kRowB + 16 * lane) = z;
+      }
     }
   }
 }
 
-// V^T fragment for the A operand of O^T += V^T P^T: two transposing LDS reads
-// (ds_read_b64_tr_b16).  Within each 16-lane group the read hands lane j
-// element (j & 3) of the 8-byte row piece addressed by lane 4t + (j >> 2) as
-// its slot t; the addresses below make lane l receive channel 32*dblk + l%32
-// of the 8 keys that the permuted reduction index assigns to its half-wave.
-__device__ __forceinline__ bf16x8 load_vt(const char* vbuf, int dblk, int c2, int lane) {
-  const int hh = lane >> 5, g = (lane >> 4) & 1, i = lane & 15, q = i & 3;
-  const int row0 = 16 * c2 + 4 * hh + (i >> 2);
-  const int chunk = 4 * dblk + 2 * g + (q >> 1);
-  const char* p0 = vbuf + lds_off(row0, chunk) + 8 * (q & 1);
-  const char* p1 = vbuf + lds_off(row0 + 8, chunk) + 8 * (q & 1);
-  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)p0);
-  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_char*)p1);
-  const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+// LDS reads of the matrix phase, issued as inline asm so that their place in
+// the instruction stream (a fixed number of steps ahead of use) and their
+// completion waits are explicit.  Addresses are byte offsets into LDS.
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
+template <int kOff>
+__device__ __forceinline__ u32x2v ds_tr(uint32_t addr) {
+  u32x2v r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
+  return r;
+}
+template <int kOff>
+__device__ __forceinline__ u32x4 ds_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
+  return r;
+}
+
+// Per-lane LDS address bases.  K fragment (kk, block kb): row 32*kb + l%32,
+// logical chunk 2*kk + l/32; with s = swz(l%32) the physical chunk is
+// 2*(kk ^ s/2) + ((l/32) ^ s)%2, so every read address is ak ^ (kk << 5)
+// plus an immediate.  V^T fragment of P*V step
+// (c2, d), half r: key row 16*c2 + 8*r + 4*hh + i/4, logical chunk
+// 4*d + 2*g + q/2 (g = bit 4 of the lane, i = lane % 16, q = i % 4); rows 8
+// apart differ only in bit 3 of the swizzle, so the address is
+// av ^ ((d ^ 2r) << 6) plus an immediate.  Within each 16-lane group the
+// transposing read hands lane j element (j & 3) of the 8-byte piece
+// addressed by lane 4t + (j >> 2) as its slot t, which makes lane l receive
+// channel 32*d + l%32 of the 8 keys the permuted reduction index assigns
+// to its half-wave.
+struct Addr {
+  uint32_t ak, av;
+};
+__device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
+  const int lr = lane & 31, hh = lane >> 5;
+  const int s = swz(lr);
+  Addr a;
+  a.ak = lds0 + lr * kRowB + 32 * (s >> 1) + 16 * ((hh ^ s) & 1);
+  const int g = (lane >> 4) & 1, i = lane & 15, q = i & 3;
+  const int row = 4 * hh + (i >> 2);
+  const int s0 = swz(row);
+  const int cl = 2 * g + (q >> 1);
+  a.av = lds0 + 2 * kTileB + row * kRowB + 64 * (s0 >> 2) + 16 * ((cl ^ s0) & 3) + 8 * (q & 1);
+  return a;
+}
+
+// K fragment of score step k (block kb = k/8, kk = k%8): block 0 is finished
+// in the first half of the matrix phase and block 1 is started in the
+// second, when the first two P chunks are no longer live.
+template <int k>
+__device__ __forceinline__ bf16x8 kfrag(const Addr& ad) {
+  constexpr int kk = k & 7, kb = k >> 3;
+  return __builtin_bit_cast(bf16x8, ds_b128<kb * 32 * kRowB>(ad.ak ^ (kk << 5)));
+}
+// V^T fragment of P*V step k (c2 = k/4, d = k%4).
+template <int k>
+__device__ __forceinline__ bf16x8 vfrag(const Addr& ad) {
+  constexpr int c2 = k >> 2, d = k & 3;
+  const u32x2v r0 = ds_tr<c2 * 16 * kRowB>(ad.av ^ (d << 6));
+  const u32x2v r1 = ds_tr<c2 * 16 * kRowB + 8 * kRowB>(ad.av ^ ((d ^ 2) << 6));
+  const u32x4 v = {r0.x, r0.y, r1.x, r1.y};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads: callers wait
+// for exactly the memory operations the next phase depends on.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct State {
+  f32x16 acc[4];
+  f32x16 s[2];
+  u32x4 ph[4], pl[4];
+  bf16x8 q[8];
+  float m_used, l_lane;
+};
+
+// S^T = K Q^T for one 64-key tile (16 MFMAs, no P*V work).
+__device__ __forceinline__ void s_only(State& st, const char* kbuf, int lane) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int kk = k >> 1, kb = k & 1;
+    const bf16x8 kv = *(const bf16x8*)(kbuf + lds_off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
+    st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
+  }
+}
+
+// Softmax of one tile: mask, row max, lazy reference-max move, p = exp2,
+// row sum, and the hi/lo BF16 split of P for the next matrix phase.
+__device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
+  if (cur_valid < kFwdBN) {
+    // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
+    const int lim = cur_valid - 4 * hh;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) st.s[kb][r] = -INFINITY;
+  }
+  float mt = st.s[0][0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, st.s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st.s[1][r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const bool move = mt > st.m_used + kTauRaw;
+  const float m_new = move ? mt : st.m_used;
+  if (__any(move)) {
+    const float alpha = (m_new == st.m_used) ? 1.0f : __builtin_amdgcn_exp2f((st.m_used - m_new) * kC);
+    st.l_lane = st.l_lane * alpha;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[d][r] = st.acc[d][r] * alpha;
+    st.m_used = m_new;
+  }
+  const float mc = st.m_used * kC;
+  float ts = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      st.s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[kb][r], kC, -mc));
+      ts = ts + st.s[kb][r];
+    }
+  st.l_lane = st.l_lane + ts;
+#pragma unroll
+  for (int c2 = 0; c2 < 4; ++c2) {
+    const int kb = c2 >> 1, r0 = 8 * (c2 & 1);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = st.s[kb][r0 + 2 * w], p1 = st.s[kb][r0 + 2 * w + 1];
+      const uint32_t u = pack_bf16x2(p0, p1);
+      st.ph[c2][w] = u;
+      st.pl[c2][w] = pack_bf16x2(p0 - bf16_lo(u), p1 - bf16_hi(u));
+    }
+  }
+}
+
+// Matrix phase: O^T += V^T P_hi^T then V^T P_lo^T per 16-key chunk, and,
+// when kS, S^T of the next tile interleaved (one score MFMA between the hi
+// and lo products).  Step k's fragments are read kPre steps ahead; sched
+// barriers pin that order and each step waits only for its own reads.
+constexpr int kPre = 2;
+
+template <bool kS, int k>
+__device__ __forceinline__ void mm_issue(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+  if constexpr (k < 16) {
+    vr[k % (kPre + 1)] = vfrag<k>(ad);
+    if constexpr (kS) kr[k % (kPre + 1)] = kfrag<k>(ad);
+  }
+}
+
+template <bool kS, int k>
+__device__ __forceinline__ void mm_step(State& st, bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+  if constexpr (k < 16) {
+    mm_issue<kS, k + kPre>(vr, kr, ad);
+    // reads issued after step k's own: those of steps k+1 .. k+kPre
+    constexpr int per = kS ? 3 : 2;
+    constexpr int ahead = (15 - k) < kPre ? (15 - k) : kPre;
+    constexpr int later = per * ahead;
+    bf16x8& vv = vr[k % (kPre + 1)];
+    bf16x8& kv = kr[k % (kPre + 1)];
+    if constexpr (kS)
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vv), "+v"(kv) : "i"(later));
+    else
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vv) : "i"(later));
+    constexpr int c2 = k >> 2, d = k & 3;
+    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.ph[c2]), st.acc[d]);
+    if constexpr (kS) st.s[k >> 3] = mfma32(kv, st.q[k & 7], st.s[k >> 3]);
+    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.pl[c2]), st.acc[d]);
+    __builtin_amdgcn_sched_barrier(0);
+    mm_step<kS, k + 1>(st, vr, kr, ad);
+  }
+}
+
+template <bool kS, int k>
+__device__ __forceinline__ void mm_prefetch(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+  if constexpr (k < kPre) {
+    mm_issue<kS, k>(vr, kr, ad);
+    mm_prefetch<kS, k + 1>(vr, kr, ad);
+  }
+}
+
+template <bool kS>
+__device__ __forceinline__ void mm_tile(State& st, const Addr& ad) {
+  if (kS) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
+  }
+  bf16x8 vr[kPre + 1], kr[kPre + 1];
+  // opaque copies: keeps the per-step address XORs inside their steps
+  Addr a2 = ad;
+  asm volatile("" : "+v"(a2.ak), "+v"(a2.av));
+  __builtin_amdgcn_sched_barrier(0);
+  mm_prefetch<kS, 0>(vr, kr, a2);
+  __builtin_amdgcn_sched_barrier(0);
+  mm_step<kS, 0>(st, vr, kr, a2);
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileB];
+  char* const kbase = smem;
+  char* const vbase = smem + 2 * kTileB;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
+  const int grp = wave >> 2, sub = wave & 3;
   const int lr = lane & 31, hh = lane >> 5;
 
-  // workgroup -> (b, h, query tile); optionally keep a head's tiles on one XCD
   int bh, qt;
   const int g = blockIdx.x;
   if (a.xcd_remap) {
@@ -155,125 +394,90 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int qrow = qt * (kFwdWaves * kFwdRowsPerWave) + wave * kFwdRowsPerWave + lr;
   const bool qvalid = qrow < a.S;
 
-  bf16x8 qreg[8];
+  State st;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     u32x4 z = {0u, 0u, 0u, 0u};
     if (qvalid) z = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
-    qreg[kk] = __builtin_bit_cast(bf16x8, z);
+    st.q[kk] = __builtin_bit_cast(bf16x8, z);
   }
-
-  const int ntxt = (L + kFwdBN - 1) / kFwdBN;
-  const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
-
-  f32x16 acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
-  float m_used = -INFINITY, l_lane = 0.f;
+    for (int r = 0; r < 16; ++r) st.acc[d][r] = 0.f;
+  st.m_used = -INFINITY;
+  st.l_lane = 0.f;
 
-  int key0, nvalid;
-  tile_bounds(0, ntxt, L, a.T_txt, a.T_img, key0, nvalid);
-  load_tile_async(a, smem, b, h, key0, nvalid, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
+  const int ntxt = (L + kFwdBN - 1) / kFwdBN;
+  const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
+  auto kbuf = [&](int j) { return kbase + (j & 1) * kTileB; };
+  auto vbuf = [&](int j) { return vbase + (j & 1) * kTileB; };
+  auto valid_of = [&](int j) {
+    int k0, nv;
+    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    return nv;
+  };
+  const RowOff ko = row_offsets(a.k.ss, lane), vo = row_offsets(a.v.ss, lane);
+  auto load_k = [&](int j) {
+    int k0, nv;
+    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
+  };
+  auto load_v = [&](int j) {
+    int k0, nv;
+    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
+  };
 
-  for (int t = 0; t < nt; ++t) {
-    const char* buf = smem + (t & 1) * kBufBytes;
-    const int cur_valid = nvalid;
-    if (t + 1 < nt) {
-      tile_bounds(t + 1, ntxt, L, a.T_txt, a.T_img, key0, nvalid);
-      load_tile_async(a, smem + ((t + 1) & 1) * kBufBytes, b, h, key0, nvalid, wave, lane);
-    }
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kv = *(const bf16x8*)(buf + lds_off(32 * kb + lr, 2 * kk + hh));
-        s[kb] = mfma32(kv, qreg[kk], s[kb]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
-    if (cur_valid < kFwdBN) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= cur_valid) s[kb][r] = -INFINITY;
-        }
-    }
-    // ---- row max (exact, any order), lane-local reference-max update
-    float mt = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool move = mt > m_used + kTauRaw;
-    const float m_new = move ? mt : m_used;
-    if (__any(move)) {
-      const float alpha = (m_new == m_used) ? 1.0f : __builtin_amdgcn_exp2f((m_used - m_new) * kC);
-      l_lane = l_lane * alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] = acc[d][r] * alpha;
-      m_used = m_new;
-    }
-    const float mc = m_used * kC;
-
-    // ---- p = exp2(s*c - m*c) in place; l sums p in FP32 in register order
-    float ts = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kC, -mc));
-        ts = ts + s[kb][r];
-      }
-    l_lane = l_lane + ts;
-
-    // ---- O^T += V^T P_hi^T, then V^T P_lo^T, one 16-key chunk at a time;
-    //      p is split into hi = bf16(p), lo = bf16(p - hi)
-    const char* vt = buf + kTileB;
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      const int kb = c2 >> 1, r0 = 8 * (c2 & 1);
-      u32x4 hw, lw;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = s[kb][r0 + 2 * w], p1 = s[kb][r0 + 2 * w + 1];
-        const uint32_t u = pack_bf16x2(p0, p1);
-        hw[w] = u;
-        lw[w] = pack_bf16x2(p0 - bf16_lo(u), p1 - bf16_hi(u));
-      }
-      const bf16x8 pbh = __builtin_bit_cast(bf16x8, hw), pbl = __builtin_bit_cast(bf16x8, lw);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 vv = load_vt(vt, d, c2, lane);
-        acc[d] = mfma32(vv, pbh, acc[d]);
-        acc[d] = mfma32(vv, pbl, acc[d]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's direct loads of the next tile have landed
-    __syncthreads();
+  // prologue: K_0, V_0 (group 0) and K_1 (group 1)
+  if (grp == 0) {
+    load_k(0);
+    load_v(0);
+  } else if (nt > 1) {
+    load_k(1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  bar();
+
+  const Addr ad = make_addr((uint32_t)(uintptr_t)(lds_char*)smem, lane);
+  // matrix phase of tile t: V_t in vbuf[t & 1], K_{t+1} in kbuf[(t + 1) & 1]
+  auto mm = [&](int t, auto ks) {
+    constexpr bool S = decltype(ks)::value;
+    Addr a2;
+    a2.av = ad.av + (t & 1) * kTileB;
+    a2.ak = ad.ak + ((t + 1) & 1) * kTileB;
+    __builtin_amdgcn_s_setprio(1);
+    mm_tile<S>(st, a2);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+
+  // Both groups run the same loop; group 1 starts one barrier later (so the
+  // two groups alternate phases), issues the tile loads and waits for them.
+  if (grp == 1) bar();
+  __builtin_amdgcn_s_setprio(1);
+  s_only(st, kbuf(0), lane);
+  __builtin_amdgcn_s_setprio(0);
+  bar();
+  for (int t = 0; t + 1 < nt; ++t) {
+    if (grp == 1) {
+      if (t + 2 < nt) load_k(t + 2);
+      load_v(t + 1);
+    }
+    softmax_tile(st, valid_of(t), hh);
+    bar();
+    mm(t, Yes{});
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
+    bar();
+  }
+  softmax_tile(st, valid_of(nt - 1), hh);
+  bar();
+  mm(nt - 1, No{});
+  if (grp == 0) bar();
 
   // ---- epilogue: O = acc / l, one RNE cast; LSE in natural log
-  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  const float l_tot = st.l_lane + __shfl_xor(st.l_lane, 32);
   if (qvalid) {
     uint16_t* orow = a.o.row(b, qrow, h);
     float* frow = a.of ? a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim : nullptr;
@@ -282,14 +486,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        const float o0 = acc[d][4 * g4] / l_tot, o1 = acc[d][4 * g4 + 1] / l_tot;
-        const float o2 = acc[d][4 * g4 + 2] / l_tot, o3 = acc[d][4 * g4 + 3] / l_tot;
+        const float o0 = st.acc[d][4 * g4] / l_tot, o1 = st.acc[d][4 * g4 + 1] / l_tot;
+        const float o2 = st.acc[d][4 * g4 + 2] / l_tot, o3 = st.acc[d][4 * g4 + 3] / l_tot;
         const u32x2 ov = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
         *(u32x2*)(orow + d0) = ov;
         if (frow) *(f32x4*)(frow + d0) = f32x4{o0, o1, o2, o3};
       }
     if (hh == 0) {
-      const float lse2 = m_used * kC + log2f(l_tot);
+      const float lse2 = st.m_used * kC + log2f(l_tot);
       a.lse[((int64_t)b * a.H + h) * a.S + qrow] = lse2 * kLn2;
     }
   }
