@@ -43,15 +43,18 @@
 //    MFMAs) and a softmax phase (VALU only), one workgroup barrier per phase,
 //    so each SIMD has one wave issuing MFMAs while its partner runs the
 //    softmax.  Group 1 starts one barrier later; both run 2*nt + 1 barriers.
-//  * LDS: K tiles in kbuf[j & 1], V tiles in vbuf[j & 1], 64 KiB.  Rows are
-//    unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key, so
-//    the K fragment reads, the transposing V reads (ds_read_b64_tr_b16, V
-//    stays row-major) and the contiguous direct-load writes avoid bank
-//    conflicts.  Group 1 fills the tiles with direct global->LDS loads
-//    (global_load_lds_dwordx4) in its softmax phase of tile t: K_{t+2} and
-//    V_{t+1}, whose buffers were last read in the matrix phases of tile
-//    t-1; it waits for them (vmcnt) at the end of its matrix phase of tile
-//    t, one barrier before group 0 reads them.
+//  * LDS: K tiles in kbuf[j % 3], V tiles in vbuf[j % 3], 96 KiB.  Rows are
+//    unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key
+//    (swizzle bits 2-3 from key bits 0-1, bits 0-1 from key bits 2-3), so
+//    the K fragment reads (16 keys per 16-lane group), the transposing V
+//    reads (ds_read_b64_tr_b16, 4 keys x 4 chunks per 32-lane group, V
+//    stays row-major) and the contiguous direct-load writes meet no LDS bank
+//    conflict on the 64 banks.  Tiles are filled by direct global->LDS loads
+//    (global_load_lds_dwordx4) issued in the softmax phase of tile t: group
+//    0 loads V_{t+1}, group 1 loads K_{t+2}; each waits for its loads
+//    (vmcnt) at the end of its next matrix phase, a barrier before the tile
+//    is read.  Three buffers are needed because group 0's softmax phase runs
+//    while group 1 still reads the tiles of tile t-1.
 //  * The matrix phase issues its LDS reads as inline asm two steps ahead of
 //    use and waits for each step's reads with an exact lgkmcnt; the direct
 //    loads are inline asm too, so the compiler neither inserts waits for
@@ -77,11 +80,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// 16-byte chunk c of key row `key` lives at chunk c ^ swz(key): conflict-free
-// for the K fragment reads (8 consecutive keys), the transposing V reads
-// (4 consecutive keys x 2 chunks) and the contiguous direct-load writes.
+// 16-byte chunk c of key row `key` lives at chunk c ^ swz(key).  swz is a
+// permutation of key % 16 (K reads: 16 consecutive keys hit 16 distinct
+// chunks) whose bits 2-3 take every value within each 4 consecutive keys
+// (transposing reads: 4 keys x 4 chunks hit 16 distinct chunks).
 __device__ __forceinline__ int swz(int key) {
-  return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8);
+  return ((key & 3) << 2) | ((key >> 2) & 3);
 }
 __device__ __forceinline__ int lds_off(int key, int chunk) {
   return key * kRowB + 16 * (chunk ^ swz(key));
@@ -180,9 +184,9 @@ __device__ __forceinline__ u32x4 ds_b128(uint32_t addr) {
 // 2*(kk ^ s/2) + ((l/32) ^ s)%2, so every read address is ak ^ (kk << 5)
 // plus an immediate.  V^T fragment of P*V step
 // (c2, d), half r: key row 16*c2 + 8*r + 4*hh + i/4, logical chunk
-// 4*d + 2*g + q/2 (g = bit 4 of the lane, i = lane % 16, q = i % 4); rows 8
-// apart differ only in bit 3 of the swizzle, so the address is
-// av ^ ((d ^ 2r) << 6) plus an immediate.  Within each 16-lane group the
+// 4*d + 2*g + q/2 (g = bit 4 of the lane, i = lane % 16, q = i % 4); the
+// physical chunk is 4*(d ^ i/4) + ((2*g + q/2) ^ (2r + hh)), so the address
+// is av ^ (d << 6) ^ (r << 5) plus an immediate.  Within each 16-lane group the
 // transposing read hands lane j element (j & 3) of the 8-byte piece
 // addressed by lane 4t + (j >> 2) as its slot t, which makes lane l receive
 // channel 32*d + l%32 of the 8 keys the permuted reduction index assigns
@@ -196,10 +200,8 @@ __device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
   Addr a;
   a.ak = lds0 + lr * kRowB + 32 * (s >> 1) + 16 * ((hh ^ s) & 1);
   const int g = (lane >> 4) & 1, i = lane & 15, q = i & 3;
-  const int row = 4 * hh + (i >> 2);
-  const int s0 = swz(row);
   const int cl = 2 * g + (q >> 1);
-  a.av = lds0 + 2 * kTileB + row * kRowB + 64 * (s0 >> 2) + 16 * ((cl ^ s0) & 3) + 8 * (q & 1);
+  a.av = lds0 + 3 * kTileB + (4 * hh + (i >> 2)) * kRowB + 64 * (i >> 2) + 16 * (cl ^ hh) + 8 * (q & 1);
   return a;
 }
 
@@ -216,7 +218,7 @@ template <int k>
 __device__ __forceinline__ bf16x8 vfrag(const Addr& ad) {
   constexpr int c2 = k >> 2, d = k & 3;
   const u32x2v r0 = ds_tr<c2 * 16 * kRowB>(ad.av ^ (d << 6));
-  const u32x2v r1 = ds_tr<c2 * 16 * kRowB + 8 * kRowB>(ad.av ^ ((d ^ 2) << 6));
+  const u32x2v r1 = ds_tr<c2 * 16 * kRowB + 8 * kRowB>(ad.av ^ (d << 6) ^ 32);
   const u32x4 v = {r0.x, r0.y, r1.x, r1.y};
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -231,8 +233,8 @@ __device__ __forceinline__ void bar() {
 
 struct State {
   f32x16 acc[4];
-  f32x16 s[2];
-  u32x4 ph[4], pl[4];
+  f32x16 s[2][2];      // two score / P buffers (tile parity), two 32-key blocks each
+  u32x4 ph[2], pl[2];  // hi/lo BF16 P of two 16-key chunks (chunk parity)
   bf16x8 q[8];
   float m_used, l_lane;
 };
@@ -242,18 +244,34 @@ __device__ __forceinline__ void s_only(State& st, const char* kbuf, int lane) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) st.s[0][kb][r] = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int kk = k >> 1, kb = k & 1;
     const bf16x8 kv = *(const bf16x8*)(kbuf + lds_off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
-    st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
+    st.s[0][kb] = mfma32(kv, st.q[kk], st.s[0][kb]);
   }
 }
 
-// Softmax of one tile: mask, row max, lazy reference-max move, p = exp2,
-// row sum, and the hi/lo BF16 split of P for the next matrix phase.
+// hi/lo BF16 split of 16-key chunk c2 of the P in buffer X, into slot c2 % 2.
+template <int X, int c2>
+__device__ __forceinline__ void pack_chunk(State& st) {
+  constexpr int kb = c2 >> 1, r0 = 8 * (c2 & 1);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float p0 = st.s[X][kb][r0 + 2 * w], p1 = st.s[X][kb][r0 + 2 * w + 1];
+    const uint32_t u = pack_bf16x2(p0, p1);
+    st.ph[c2 & 1][w] = u;
+    st.pl[c2 & 1][w] = pack_bf16x2(p0 - bf16_lo(u), p1 - bf16_hi(u));
+  }
+}
+
+// Softmax of one tile (scores in buffer X, replaced by P in place): mask, row
+// max, lazy reference-max move, p = exp2, row sum; then the hi/lo split of
+// the first 16-key chunk (the matrix phase splits the others one chunk ahead).
+template <int X>
 __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
+  f32x16 (&sx)[2] = st.s[X];
   if (cur_valid < kFwdBN) {
     // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
     const int lim = cur_valid - 4 * hh;
@@ -261,13 +279,13 @@ __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) st.s[kb][r] = -INFINITY;
+        if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sx[kb][r] = -INFINITY;
   }
-  float mt = st.s[0][0];
+  float mt = sx[0][0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, st.s[0][r]);
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sx[0][r]);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st.s[1][r]);
+  for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[1][r]);
   mt = fmaxf(mt, __shfl_xor(mt, 32));
   const bool move = mt > st.m_used + kTauRaw;
   const float m_new = move ? mt : st.m_used;
@@ -286,21 +304,11 @@ __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      st.s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[kb][r], kC, -mc));
-      ts = ts + st.s[kb][r];
+      sx[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[kb][r], kC, -mc));
+      ts = ts + sx[kb][r];
     }
   st.l_lane = st.l_lane + ts;
-#pragma unroll
-  for (int c2 = 0; c2 < 4; ++c2) {
-    const int kb = c2 >> 1, r0 = 8 * (c2 & 1);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = st.s[kb][r0 + 2 * w], p1 = st.s[kb][r0 + 2 * w + 1];
-      const uint32_t u = pack_bf16x2(p0, p1);
-      st.ph[c2][w] = u;
-      st.pl[c2][w] = pack_bf16x2(p0 - bf16_lo(u), p1 - bf16_hi(u));
-    }
-  }
+  pack_chunk<X, 0>(st);
 }
 
 // Matrix phase: O^T += V^T P_hi^T then V^T P_lo^T per 16-key chunk, and,
@@ -317,7 +325,7 @@ __device__ __forceinline__ void mm_issue(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kP
   }
 }
 
-template <bool kS, int k>
+template <bool kS, int X, int k>
 __device__ __forceinline__ void mm_step(State& st, bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
   if constexpr (k < 16) {
     mm_issue<kS, k + kPre>(vr, kr, ad);
@@ -332,11 +340,13 @@ __device__ __forceinline__ void mm_step(State& st, bf16x8 (&vr)[kPre + 1], bf16x
     else
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vv) : "i"(later));
     constexpr int c2 = k >> 2, d = k & 3;
-    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.ph[c2]), st.acc[d]);
-    if constexpr (kS) st.s[k >> 3] = mfma32(kv, st.q[k & 7], st.s[k >> 3]);
-    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.pl[c2]), st.acc[d]);
+    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.ph[c2 & 1]), st.acc[d]);
+    if constexpr (kS) st.s[1 - X][k >> 3] = mfma32(kv, st.q[k & 7], st.s[1 - X][k >> 3]);
+    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.pl[c2 & 1]), st.acc[d]);
+    // split the next chunk while this chunk's products run
+    if constexpr ((k & 3) == 1 && c2 < 3) pack_chunk<X, c2 + 1>(st);
     __builtin_amdgcn_sched_barrier(0);
-    mm_step<kS, k + 1>(st, vr, kr, ad);
+    mm_step<kS, X, k + 1>(st, vr, kr, ad);
   }
 }
 
@@ -348,13 +358,13 @@ __device__ __forceinline__ void mm_prefetch(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)
   }
 }
 
-template <bool kS>
+template <bool kS, int X>
 __device__ __forceinline__ void mm_tile(State& st, const Addr& ad) {
   if (kS) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st.s[1 - X][kb][r] = 0.f;
   }
   bf16x8 vr[kPre + 1], kr[kPre + 1];
   // opaque copies: keeps the per-step address XORs inside their steps
@@ -363,15 +373,15 @@ __device__ __forceinline__ void mm_tile(State& st, const Addr& ad) {
   __builtin_amdgcn_sched_barrier(0);
   mm_prefetch<kS, 0>(vr, kr, a2);
   __builtin_amdgcn_sched_barrier(0);
-  mm_step<kS, 0>(st, vr, kr, a2);
+  mm_step<kS, X, 0>(st, vr, kr, a2);
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileB];
+  __shared__ __attribute__((aligned(1024))) char smem[6 * kTileB];
   char* const kbase = smem;
-  char* const vbase = smem + 2 * kTileB;
+  char* const vbase = smem + 3 * kTileB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
@@ -410,8 +420,8 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
 
   const int ntxt = (L + kFwdBN - 1) / kFwdBN;
   const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
-  auto kbuf = [&](int j) { return kbase + (j & 1) * kTileB; };
-  auto vbuf = [&](int j) { return vbase + (j & 1) * kTileB; };
+  auto kbuf = [&](int j) { return kbase + (j % 3) * kTileB; };
+  auto vbuf = [&](int j) { return vbase + (j % 3) * kTileB; };
   auto valid_of = [&](int j) {
     int k0, nv;
     tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
@@ -440,41 +450,63 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   bar();
 
   const Addr ad = make_addr((uint32_t)(uintptr_t)(lds_char*)smem, lane);
-  // matrix phase of tile t: V_t in vbuf[t & 1], K_{t+1} in kbuf[(t + 1) & 1]
-  auto mm = [&](int t, auto ks) {
+  // matrix phase of tile t: V_t in vbuf[t % 3], K_{t+1} in kbuf[(t + 1) % 3];
+  // P of tile t in score buffer t & 1, scores of tile t+1 into the other
+  auto mm = [&](int t, auto par, auto ks) {
+    constexpr int X = decltype(par)::value;
     constexpr bool S = decltype(ks)::value;
     Addr a2;
-    a2.av = ad.av + (t & 1) * kTileB;
-    a2.ak = ad.ak + ((t + 1) & 1) * kTileB;
+    a2.av = ad.av + (t % 3) * kTileB;
+    a2.ak = ad.ak + ((t + 1) % 3) * kTileB;
     __builtin_amdgcn_s_setprio(1);
-    mm_tile<S>(st, a2);
+    mm_tile<S, X>(st, a2);
     __builtin_amdgcn_s_setprio(0);
   };
   using Yes = std::true_type;
   using No = std::false_type;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // one tile with a successor: group 0 loads V_{t+1}, group 1 K_{t+2};
+  // softmax; matrix phase; each group waits for its own loads
+  auto tile = [&](int t, auto par) {
+    constexpr int X = decltype(par)::value;
+    if (grp == 1) {
+      if (t + 2 < nt) load_k(t + 2);
+    } else {
+      load_v(t + 1);
+    }
+    softmax_tile<X>(st, valid_of(t), hh);
+    bar();
+    mm(t, par, Yes{});
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
+    bar();
+  };
+  auto last = [&](int t, auto par) {
+    constexpr int X = decltype(par)::value;
+    softmax_tile<X>(st, valid_of(t), hh);
+    bar();
+    mm(t, par, No{});
+    if (grp == 0) bar();
+  };
 
-  // Both groups run the same loop; group 1 starts one barrier later (so the
-  // two groups alternate phases), issues the tile loads and waits for them.
+  // Both groups run the same sequence; group 1 starts one barrier later, so
+  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
   if (grp == 1) bar();
   __builtin_amdgcn_s_setprio(1);
   s_only(st, kbuf(0), lane);
   __builtin_amdgcn_s_setprio(0);
   bar();
-  for (int t = 0; t + 1 < nt; ++t) {
-    if (grp == 1) {
-      if (t + 2 < nt) load_k(t + 2);
-      load_v(t + 1);
-    }
-    softmax_tile(st, valid_of(t), hh);
-    bar();
-    mm(t, Yes{});
-    if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
-    bar();
+  int t = 0;
+  for (; t + 2 < nt; t += 2) {
+    tile(t, B0{});
+    tile(t + 1, B1{});
   }
-  softmax_tile(st, valid_of(nt - 1), hh);
-  bar();
-  mm(nt - 1, No{});
-  if (grp == 0) bar();
+  if (t + 1 < nt) {
+    tile(t, B0{});
+    last(t + 1, B1{});
+  } else {
+    last(t, B0{});
+  }
 
   // ---- epilogue: O = acc / l, one RNE cast; LSE in natural log
   const float l_tot = st.l_lane + __shfl_xor(st.l_lane, 32);
