@@ -405,7 +405,9 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
 
   char* ws = (char*)workspace;
   float* Dvec = (float*)(ws + Lw.dvec);
-  const int rows_per_wg = 128;
+  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride))
+    return fail(QI_E_UNSUPPORTED, "k/v sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  const int rows_per_wg = kBwdDqWaves * 32;
   int nk_max = 0;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
@@ -435,7 +437,7 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.n_ktiles = nk_max;
     a.xcd_remap = ((nb * geom->H) % 8) == 0;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(kBwdDqWaves * 64), 0,
                        stream, a);
     if ((rc = launched("attn_bwd_dq_kernel"))) return rc;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_ktiles)), dim3(256), 0,

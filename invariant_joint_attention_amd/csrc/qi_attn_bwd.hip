@@ -28,6 +28,7 @@
 // 16-chunk swapped) to match the accumulator layout of the probabilities.
 #include "qi_common.h"
 #include "qi_kernels.h"
+#include "qi_lds.h"
 
 namespace qi {
 
@@ -95,24 +96,155 @@ __device__ __forceinline__ void decode_bh(const BwdArgs& a, int ntiles, int& b, 
 }
 
 // ----------------------------------------------------------------- dQ pass
-constexpr int kQK = kBwdBN * kRow;        // K row-major
-constexpr int kQV = kBwdBN * kRow;        // V row-major
-constexpr int kQKT = kHeadDim * kTRow;    // K^T
-constexpr int kQBuf = kQK + kQV + kQKT;   // 53248
+// Workgroup = 8 waves x 32 query rows of one (b, h); waves w and w+4 share a
+// SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) alternate, one barrier
+// per phase, between a matrix phase (dQ^T += K_t^T dS_t^T with dS split
+// hi/lo, then the scores and dP of tile t+1: 64 MFMAs) and a VALU phase
+// (P, dS and its split for tile t+1).  K and V tiles are triple-buffered in
+// LDS (96 KiB) and filled by direct loads: in its VALU phase of tile t group
+// 0 loads V_{t+2} and group 1 K_{t+2}; each waits for its loads at the end
+// of its next matrix phase.  The arithmetic is the frozen one of the pass
+// (per accumulator: scores and dP over the 8 head-dim chunks in order, dQ
+// over the 16-key chunks in key order, hi then lo).
+using namespace lds;
+static_assert(kTileRows == kBwdBN, "dQ key tile is one LDS tile");
+
+struct DqState {
+  f32x16 acc[4];       // dQ^T: 4 head-dim blocks x 32 queries
+  f32x16 s[2], dp[2];  // S^T and dP^T of one tile (two 32-key blocks)
+  u32x4 dh[4], dl[4];  // hi / lo BF16 dS^T of the four 16-key chunks
+  bf16x8 q[8], o[8];   // Q and dO rows of the wave's 32 queries
+  float lse2, D;
+};
+
+__device__ __forceinline__ void dq_bounds(int t, int ntxt, int L, int T_txt, int T_img, int& key0, int& nvalid) {
+  if (t < ntxt) {
+    key0 = t * kBwdBN;
+    nvalid = min(kBwdBN, L - key0);
+  } else {
+    const int ti = t - ntxt;
+    key0 = T_txt + ti * kBwdBN;
+    nvalid = min(kBwdBN, T_img - ti * kBwdBN);
+  }
+}
+
+// P = exp2(s*c - LSE*log2 e) (0 for masked keys), dS = P (dP - D), split
+// into hi = bf16(dS), lo = bf16(dS - hi) per 16-key chunk.
+__device__ __forceinline__ void dq_softmax(DqState& st, int cur_valid, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
+      const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float p = key < cur_valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[kb][r], kC, -st.lse2)) : 0.f;
+      ds[r] = p * (st.dp[kb][r] - st.D);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t hi[4], lo[4];
+      split_pack(ds + 8 * half, hi, lo);
+      st.dh[2 * kb + half] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      st.dl[2 * kb + half] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+  }
+}
+
+// Matrix phase, 4 LDS reads and 4 MFMAs per step, fragments read one step
+// ahead.  dQ steps j = 0..7: chunk c2 = j/2, head-dim blocks 2(j%2) and
+// 2(j%2)+1 from the transposed K_t tile.  Score steps j = 0..7: head-dim
+// chunk kk = j of both 32-key blocks of S^T (K_{t+1}) and dP^T (V_{t+1}).
+struct DqBases {
+  uint32_t tk, rk, rv;  // K_t transposed, K_{t+1} rows, V_{t+1} rows
+};
+using Ring = bf16x8[2][4];
+
+template <bool kDq, int k>
+__device__ __forceinline__ void dq_issue(Ring& f, const DqBases& b) {
+  constexpr int nsteps = (kDq ? 8 : 0) + 8;
+  if constexpr (k < nsteps) {
+    bf16x8* x = f[k & 1];
+    if constexpr (kDq && k < 8) {
+      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
+      x[0] = tr_frag<c2, d0>(b.tk);
+      x[1] = tr_frag<c2, d1>(b.tk);
+    } else {
+      constexpr int kk = kDq ? k - 8 : k;
+      x[0] = row_frag<kk, 0>(b.rk);
+      x[1] = row_frag<kk, 0>(b.rv);
+      x[2] = row_frag<kk, 1>(b.rk);
+      x[3] = row_frag<kk, 1>(b.rv);
+    }
+  }
+}
+
+template <bool kDq, bool kS, int k>
+__device__ __forceinline__ void dq_step(DqState& st, Ring& f, const DqBases& b) {
+  constexpr int nsteps = (kDq ? 8 : 0) + (kS ? 8 : 0);
+  if constexpr (k < nsteps) {
+    if constexpr (!(kDq && !kS && k + 1 >= 8)) dq_issue<kDq, k + 1>(f, b);
+    // LDS reads issued after this step's: the next step's 4
+    constexpr int later = (k + 1 < nsteps) ? 4 : 0;
+    bf16x8* x = f[k & 1];
+    if constexpr (kDq && k < 8) {
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
+      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
+      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d0]);
+      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d1]);
+      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d0]);
+      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(later));
+      constexpr int kk = kDq ? k - 8 : k;
+      st.s[0] = mfma32(x[0], st.q[kk], st.s[0]);
+      st.dp[0] = mfma32(x[1], st.o[kk], st.dp[0]);
+      st.s[1] = mfma32(x[2], st.q[kk], st.s[1]);
+      st.dp[1] = mfma32(x[3], st.o[kk], st.dp[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    dq_step<kDq, kS, k + 1>(st, f, b);
+  }
+}
+
+template <bool kDq, bool kS>
+__device__ __forceinline__ void dq_matrix(DqState& st, DqBases b) {
+  if (kS) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.s[kb][r] = 0.f;
+        st.dp[kb][r] = 0.f;
+      }
+  }
+  Ring f;
+  // opaque copies keep the per-step address XORs inside their steps
+  asm volatile("" : "+v"(b.tk), "+v"(b.rk), "+v"(b.rv));
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kDq)
+    dq_issue<true, 0>(f, b);
+  else
+    dq_issue<false, 0>(f, b);
+  __builtin_amdgcn_sched_barrier(0);
+  dq_step<kDq, kS, 0>(st, f, b);
+}
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kQBuf];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[6 * kTileB];  // K tiles [3], V tiles [3]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, sub = wave & 3;
   const int lr = lane & 31, hh = lane >> 5;
   int b, h, qt;
   decode_bh(a, a.n_qtiles, b, h, qt);
   const int L = a.txt_len[b];
-  const int qrow = qt * 128 + wave * 32 + lr;
+  const int qrow = qt * (kBwdDqWaves * 32) + wave * 32 + lr;
   const bool qvalid = qrow < a.S;
 
-  bf16x8 qreg[8], dreg[8];
+  DqState st;
   float dpart = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -125,8 +257,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
       o0 = *(const f32x4*)orow;
       o1 = *(const f32x4*)(orow + 4);
     }
-    qreg[kk] = __builtin_bit_cast(bf16x8, zq);
-    dreg[kk] = __builtin_bit_cast(bf16x8, zd);
+    st.q[kk] = __builtin_bit_cast(bf16x8, zq);
+    st.o[kk] = __builtin_bit_cast(bf16x8, zd);
+    // D_i = dO_i . O_i (FP32 pre-cast O), fixed order: chunk, then channel
     const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -136,100 +269,100 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
       dpart = dpart + p1;
     }
   }
-  const float Dq = dpart + __shfl_xor(dpart, 32);
-  float lse2 = INFINITY;
+  st.D = dpart + __shfl_xor(dpart, 32);
+  st.lse2 = INFINITY;
   if (qvalid) {
     const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
-    lse2 = a.lse[li] * kLog2e;
-    if (hh == 0) a.Dvec[li] = Dq;
+    st.lse2 = a.lse[li] * kLog2e;
+    if (hh == 0) a.Dvec[li] = st.D;
   }
-
-  const int ntxt = (L + kBwdBN - 1) / kBwdBN;
-  const int nt = ntxt + (a.T_img + kBwdBN - 1) / kBwdBN;
-
-  f32x16 acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+    for (int r = 0; r < 16; ++r) st.acc[d][r] = 0.f;
 
-  const int tid = threadIdx.x, a4 = tid >> 4, c16 = tid & 15;
-  u32x4 kr[4], vr[4];
-  auto bounds = [&](int t, int& key0, int& nv) {
-    if (t < ntxt) { key0 = t * kBwdBN; nv = min(kBwdBN, L - key0); }
-    else { const int ti = t - ntxt; key0 = a.T_txt + ti * kBwdBN; nv = min(kBwdBN, a.T_img - ti * kBwdBN); }
+  const int ntxt = (L + kBwdBN - 1) / kBwdBN;
+  const int nt = ntxt + (a.T_img + kBwdBN - 1) / kBwdBN;
+  char* const kbase = smem;
+  char* const vbase = smem + 3 * kTileB;
+  auto kbuf = [&](int j) { return kbase + (j % 3) * kTileB; };
+  auto vbuf = [&](int j) { return vbase + (j % 3) * kTileB; };
+  auto valid_of = [&](int j) {
+    int k0, nv;
+    dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    return nv;
   };
-  auto load = [&](int key0, int nv) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 4 * a4 + r;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < nv) {
-        zk = *(const u32x4*)(a.k.row(b, key0 + key, h) + 8 * c16);
-        zv = *(const u32x4*)(a.v.row(b, key0 + key, h) + 8 * c16);
-      }
-      kr[r] = zk;
-      vr[r] = zv;
-    }
+  const RowOff ko = row_offsets(a.k.ss, lane), vo = row_offsets(a.v.ss, lane);
+  auto load_k = [&](int j) {
+    int k0, nv;
+    dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
   };
-  auto store = [&](char* buf) {
-    store_rows_and_t(buf, buf + kQK + kQV, kr, a4, c16);
-    store_rows_and_t(buf + kQK, nullptr, vr, a4, c16);
+  auto load_v = [&](int j) {
+    int k0, nv;
+    dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
+  };
+  auto bases = [&](int t) {
+    DqBases bb;
+    bb.tk = tr_base(addr_of(kbuf(t)), lane);
+    bb.rk = row_base(addr_of(kbuf(t + 1)), lane);
+    bb.rv = row_base(addr_of(vbuf(t + 1)), lane);
+    return bb;
   };
 
-  int key0, nv;
-  bounds(0, key0, nv);
-  load(key0, nv);
-  store(smem);
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const char* buf = smem + (t & 1) * kQBuf;
-    const int cur_valid = nv;
-    if (t + 1 < nt) {
-      bounds(t + 1, key0, nv);
-      load(key0, nv);
-    }
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = (32 * kb + lr) * kRow + (16 * kk + 8 * hh) * 2;
-        s[kb] = mfma32(*(const bf16x8*)(buf + off), qreg[kk], s[kb]);
-        dp[kb] = mfma32(*(const bf16x8*)(buf + kQK + off), dreg[kk], dp[kb]);
-      }
-    uint32_t hi[2][8], lo[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const float p = key < cur_valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kC, -lse2)) : 0.f;
-        ds[r] = p * (dp[kb][r] - Dq);
-      }
-      split_pack(ds, hi[kb], lo[kb]);
-      split_pack(ds + 8, hi[kb] + 4, lo[kb] + 4);
-    }
-    const char* kt = buf + kQK + kQV;
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      const int kb = c2 >> 1, half = c2 & 1;
-      const bf16x8 bh_ = as_bf16x8(hi[kb] + 4 * half), bl_ = as_bf16x8(lo[kb] + 4 * half);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 av = *(const bf16x8*)(kt + (32 * d + lr) * kTRow + (16 * c2 + 8 * hh) * 2);
-        acc[d] = mfma32(av, bh_, acc[d]);
-        acc[d] = mfma32(av, bl_, acc[d]);
-      }
-    }
-    if (t + 1 < nt) store(smem + ((t + 1) & 1) * kQBuf);
-    __syncthreads();
+  // prologue: tiles 0 (group 0) and 1 (group 1)
+  if (grp == 0) {
+    load_k(0);
+    load_v(0);
+  } else if (nt > 1) {
+    load_k(1);
+    load_v(1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  bar();
+
+  // Both groups run the same sequence; group 1 starts one barrier later, so
+  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
+  if (grp == 1) bar();
+  {
+    DqBases b0;
+    b0.tk = 0;
+    b0.rk = row_base(addr_of(kbuf(0)), lane);
+    b0.rv = row_base(addr_of(vbuf(0)), lane);
+    __builtin_amdgcn_s_setprio(1);
+    dq_matrix<false, true>(st, b0);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  bar();
+  for (int t = 0; t + 1 < nt; ++t) {
+    if (t + 2 < nt) {
+      if (grp == 0)
+        load_v(t + 2);
+      else
+        load_k(t + 2);
+    }
+    dq_softmax(st, valid_of(t), hh);
+    bar();
+    __builtin_amdgcn_s_setprio(1);
+    dq_matrix<true, true>(st, bases(t));
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
+    bar();
+  }
+  dq_softmax(st, valid_of(nt - 1), hh);
+  bar();
+  {
+    DqBases bl;
+    bl.tk = tr_base(addr_of(kbuf(nt - 1)), lane);
+    bl.rk = 0;
+    bl.rv = 0;
+    __builtin_amdgcn_s_setprio(1);
+    dq_matrix<true, false>(st, bl);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  if (grp == 0) bar();
+
   if (qvalid) {
     float* drow = a.dq.row(b, qrow, h);
 #pragma unroll
@@ -237,8 +370,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        *(f32x4*)(drow + d0) = f32x4{acc[d][4 * g4] * kScale, acc[d][4 * g4 + 1] * kScale,
-                                     acc[d][4 * g4 + 2] * kScale, acc[d][4 * g4 + 3] * kScale};
+        *(f32x4*)(drow + d0) = f32x4{st.acc[d][4 * g4] * kScale, st.acc[d][4 * g4 + 1] * kScale,
+                                     st.acc[d][4 * g4 + 2] * kScale, st.acc[d][4 * g4 + 3] * kScale};
       }
   }
 }

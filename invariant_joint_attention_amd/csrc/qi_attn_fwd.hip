@@ -61,6 +61,7 @@
 //    them before unrelated LDS reads nor keeps 64-bit addresses for them.
 #include "qi_common.h"
 #include "qi_kernels.h"
+#include "qi_lds.h"
 
 #include <type_traits>
 
@@ -68,28 +69,13 @@ namespace qi {
 
 namespace {
 
-constexpr int kRowB = 256;                   // bytes per K / V row in LDS (unpadded, chunk-swizzled)
-constexpr int kTileB = kFwdBN * kRowB;       // 16384
+using namespace lds;
+static_assert(kTileRows == kFwdBN, "forward key tile is one LDS tile");
 // log2(e) / sqrt(128), rounded once to FP32
 constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);
 constexpr float kLn2 = 0.69314718055994530942f;
 // Threshold on raw scores for moving the reference max: 8 in the exp2 domain.
 constexpr float kTauRaw = (float)(8.0 / (1.4426950408889634074 / 11.313708498984760390));
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// 16-byte chunk c of key row `key` lives at chunk c ^ swz(key).  swz is a
-// permutation of key % 16 (K reads: 16 consecutive keys hit 16 distinct
-// chunks) whose bits 2-3 take every value within each 4 consecutive keys
-// (transposing reads: 4 keys x 4 chunks hit 16 distinct chunks).
-__device__ __forceinline__ int swz(int key) {
-  return ((key & 3) << 2) | ((key >> 2) & 3);
-}
-__device__ __forceinline__ int lds_off(int key, int chunk) {
-  return key * kRowB + 16 * (chunk ^ swz(key));
-}
 
 __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, int T_img, int& key0,
                                             int& nvalid) {
@@ -103,105 +89,15 @@ __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, i
   }
 }
 
-// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4
-// with a scalar base and a 32-bit lane offset): lane l's bytes land at LDS
-// byte lds + 16*l.  Issued as inline asm, so the compiler neither waits for
-// it before unrelated LDS reads nor spills 64-bit addresses for it; the
-// kernel waits for these loads explicitly (vmcnt) before the barrier that
-// publishes the tile.  M0 (the LDS destination) is written here and has no
-// other user in this kernel: no LDS-DMA builtin, GWS or message send, so the
-// compiler keeps nothing in it that the clobber could destroy.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(off), "s"(base)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Global -> LDS tile fill: wave `sub` of a group fills keys 16*sub..16*sub+15
-// of one 64-key tile, 4 keys (1 KiB) per instruction; lane l writes LDS slot
-// l of the instruction's block, i.e. physical chunk l%16 of key 4i + l/16,
-// so it fetches the logical chunk that the swizzle maps there.  Keys past
-// the tile's valid count are not read; their slots are zero-filled so a
-// masked key never contributes a NaN.
-struct RowOff {
-  uint32_t o[4];
-};
-__device__ __forceinline__ RowOff row_offsets(int64_t ss, int lane) {
-  RowOff r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kl = 4 * i + (lane >> 4);       // key within a wave's 16
-    const int chunk = (lane & 15) ^ swz(kl);  // swz depends on key % 16 only
-    r.o[i] = (uint32_t)(kl * (uint32_t)ss + 8 * chunk) * 2u;
-  }
-  return r;
-}
-__device__ __forceinline__ void load_rows(const View<const uint16_t>& src, const RowOff& ro, char* dst, int b,
-                                          int h, int key0, int nvalid, int sub, int lane) {
-  const char* base = (const char*)(src.p + (int64_t)b * src.sb + (int64_t)h * src.sh +
-                                   (int64_t)(key0 + 16 * sub) * src.ss);
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(dst + 16 * sub * kRowB);
-  if (nvalid >= 16 * sub + 16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(base, ro.o[i], lds + 4 * i * kRowB);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (16 * sub + 4 * i + (lane >> 4) < nvalid) {
-        dma16(base, ro.o[i], lds + 4 * i * kRowB);
-      } else {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *(u32x4*)(dst + (16 * sub + 4 * i) * kRowB + 16 * lane) = z;
-      }
-    }
-  }
-}
-
-// LDS reads of the matrix phase, issued as inline asm so that their place in
-// the instruction stream (a fixed number of steps ahead of use) and their
-// completion waits are explicit.  Addresses are byte offsets into LDS.
-typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-
-template <int kOff>
-__device__ __forceinline__ u32x2v ds_tr(uint32_t addr) {
-  u32x2v r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
-  return r;
-}
-template <int kOff>
-__device__ __forceinline__ u32x4 ds_b128(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
-  return r;
-}
-
-// Per-lane LDS address bases.  K fragment (kk, block kb): row 32*kb + l%32,
-// logical chunk 2*kk + l/32; with s = swz(l%32) the physical chunk is
-// 2*(kk ^ s/2) + ((l/32) ^ s)%2, so every read address is ak ^ (kk << 5)
-// plus an immediate.  V^T fragment of P*V step
-// (c2, d), half r: key row 16*c2 + 8*r + 4*hh + i/4, logical chunk
-// 4*d + 2*g + q/2 (g = bit 4 of the lane, i = lane % 16, q = i % 4); the
-// physical chunk is 4*(d ^ i/4) + ((2*g + q/2) ^ (2r + hh)), so the address
-// is av ^ (d << 6) ^ (r << 5) plus an immediate.  Within each 16-lane group the
-// transposing read hands lane j element (j & 3) of the 8-byte piece
-// addressed by lane 4t + (j >> 2) as its slot t, which makes lane l receive
-// channel 32*d + l%32 of the 8 keys the permuted reduction index assigns
-// to its half-wave.
+// Per-lane LDS bases of the matrix phase: K row fragments (scores) and V
+// transposed fragments (P*V).
 struct Addr {
   uint32_t ak, av;
 };
 __device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
-  const int lr = lane & 31, hh = lane >> 5;
-  const int s = swz(lr);
   Addr a;
-  a.ak = lds0 + lr * kRowB + 32 * (s >> 1) + 16 * ((hh ^ s) & 1);
-  const int g = (lane >> 4) & 1, i = lane & 15, q = i & 3;
-  const int cl = 2 * g + (q >> 1);
-  a.av = lds0 + 3 * kTileB + (4 * hh + (i >> 2)) * kRowB + 64 * (i >> 2) + 16 * (cl ^ hh) + 8 * (q & 1);
+  a.ak = row_base(lds0, lane);
+  a.av = tr_base(lds0 + 3 * kTileB, lane);
   return a;
 }
 
@@ -211,24 +107,13 @@ __device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
 template <int k>
 __device__ __forceinline__ bf16x8 kfrag(const Addr& ad) {
   constexpr int kk = k & 7, kb = k >> 3;
-  return __builtin_bit_cast(bf16x8, ds_b128<kb * 32 * kRowB>(ad.ak ^ (kk << 5)));
+  return lds::row_frag<kk, kb>(ad.ak);
 }
 // V^T fragment of P*V step k (c2 = k/4, d = k%4).
 template <int k>
 __device__ __forceinline__ bf16x8 vfrag(const Addr& ad) {
   constexpr int c2 = k >> 2, d = k & 3;
-  const u32x2v r0 = ds_tr<c2 * 16 * kRowB>(ad.av ^ (d << 6));
-  const u32x2v r1 = ds_tr<c2 * 16 * kRowB + 8 * kRowB>(ad.av ^ (d << 6) ^ 32);
-  const u32x4 v = {r0.x, r0.y, r1.x, r1.y};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Workgroup barrier without the memory fence of __syncthreads: callers wait
-// for exactly the memory operations the next phase depends on.
-__device__ __forceinline__ void bar() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  return lds::tr_frag<c2, d>(ad.av);
 }
 
 struct State {
@@ -248,7 +133,7 @@ __device__ __forceinline__ void s_only(State& st, const char* kbuf, int lane) {
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int kk = k >> 1, kb = k & 1;
-    const bf16x8 kv = *(const bf16x8*)(kbuf + lds_off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
+    const bf16x8 kv = *(const bf16x8*)(kbuf + off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
     st.s[0][kb] = mfma32(kv, st.q[kk], st.s[0][kb]);
   }
 }

@@ -58,6 +58,7 @@ struct FwdArgs {
 // Backward attention.
 constexpr int kBwdBN = 64;  // key tile of the dQ pass (= forward order)
 constexpr int kBwdBM = 64;  // query tile of the dK/dV pass (frozen)
+constexpr int kBwdDqWaves = 8;  // dQ pass: waves per workgroup (two alternating groups of 4)
 
 struct BwdArgs {
   View<const uint16_t> q, k, v, dO;

@@ -268,8 +268,19 @@ __global__ __launch_bounds__(128) void dgain_fold_kernel(DgainFoldArgs a) {
   }
   float tot = 0.f;
   for (int b = 0; b < a.B; ++b) {
+    // The adds run in ascending chunk order; the loads of a batch of 32
+    // chunks are all issued before its adds, so the chain waits on memory
+    // once per batch instead of once per chunk.
+    const float* src = a.partials + (int64_t)b * a.n_chunks * kHeadDim + cc;
     float v = 0.f;
-    for (int kk = k0; kk < k1; ++kk) v = v + a.partials[((int64_t)b * a.n_chunks + kk) * kHeadDim + cc];
+    for (int kk = k0; kk < k1; kk += 32) {
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = kk + j < k1 ? src[(int64_t)(kk + j) * kHeadDim] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (kk + j < k1) v = v + x[j];
+    }
     a.dg_ps[((int64_t)b * a.gain_streams + set) * kHeadDim + cc] = v;
     tot = tot + v;
   }
