@@ -405,9 +405,11 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
 
   char* ws = (char*)workspace;
   float* Dvec = (float*)(ws + Lw.dvec);
-  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride))
-    return fail(QI_E_UNSUPPORTED, "k/v sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride || q.ss > kFwdMaxRowStride ||
+                d_o.ss > kFwdMaxRowStride))
+    return fail(QI_E_UNSUPPORTED, "q/k/v/d_o sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   const int rows_per_wg = kBwdDqWaves * 32;
+  const int keys_per_wg = kBwdKvWaves * 32;
   int nk_max = 0;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
@@ -431,7 +433,8 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     nk_max = 0;
     for (int i = 0; i < nb; ++i) {
       const int L = geom->txt_len[b0 + i];
-      const int nk = (int)(ceil_div(L, 128) + ceil_div(a.T_img, 128) + ceil_div(geom->T_txt - L, 128));
+      const int nk = (int)(ceil_div(L, keys_per_wg) + ceil_div(a.T_img, keys_per_wg) +
+                           ceil_div(geom->T_txt - L, keys_per_wg));
       nk_max = std::max(nk_max, nk);
     }
     a.n_ktiles = nk_max;
@@ -440,9 +443,11 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(kBwdDqWaves * 64), 0,
                        stream, a);
     if ((rc = launched("attn_bwd_dq_kernel"))) return rc;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_ktiles)), dim3(256), 0,
-                       stream, a);
-    if ((rc = launched("attn_bwd_dkdv_kernel"))) return rc;
+    const dim3 kv_grid((unsigned)((int64_t)nb * geom->H * a.n_ktiles));
+    hipLaunchKernelGGL(attn_bwd_dk_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
+    if ((rc = launched("attn_bwd_dk_kernel"))) return rc;
+    hipLaunchKernelGGL(attn_bwd_dv_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
+    if ((rc = launched("attn_bwd_dv_kernel"))) return rc;
   }
   if ((rc = launch_prologue_bwd(geom, q_raw, gain_q, dq, (float*)(ws + Lw.pq), dgain_q_ps, dgain_q, Lw, stream)))
     return rc;
@@ -456,7 +461,8 @@ const char* qi_trace(void) {
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":1,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
              "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
-             "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dkdv\":\"attn_bwd_dkdv_kernel\"},"
+             "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
+             "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16\",\"accumulator\":\"fp32\","
              "\"frozen\":{\"fwd_key_tile\":%d,\"bwd_dq_key_tile\":%d,\"bwd_dkdv_query_tile\":%d,"
              "\"prologue_dgain_chunk\":%d,\"key_order\":\"text tiles from 0, image tiles from T_txt\","

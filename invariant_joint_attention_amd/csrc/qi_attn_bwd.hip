@@ -6,26 +6,35 @@
 // trees, FP32 accumulators, no atomics); [Kernel list] "[RFC] [Qwen-Image]
 // WS1 Single-GPU Kernel List", rows joint_attn_* (forward and backward).
 //
-// Two passes, each output element written by exactly one lane, no atomics:
+// Three passes, each output element written by exactly one lane, no atomics:
 //  * dQ pass (query-tile-major, grid as the forward): per wave 32 queries.
 //    D_i = dO_i . O_i is formed first (fixed order) from the forward's FP32
 //    (pre-cast) O -- the BF16 O would move D by ~2^-9 |dO||O| sqrt(128), which
 //    the gain gradients, sums of many cancelling rows, do not tolerate -- and
-//    stored for the dK/dV pass.  Then over the key tiles in the forward's logical order:
-//    S^T = K Q^T, dP^T = V dO^T, P = exp2(s*c - LSE*log2 e),
-//    dS = P (dP - D), dQ^T += K^T dS^T with dS split into two BF16 terms
-//    (hi = bf16(dS), lo = bf16(dS - hi)) accumulated hi then lo.
-//  * dK/dV pass (key-tile-major): per wave 32 keys held in registers.  Query
-//    tiles of 64 rows are visited in a frozen logical order -- valid text rows
-//    from 0, image rows from T_txt, then padded text rows from L_b -- so the
-//    sum over queries of a key never depends on the batch or the launch.
-//    S = Q K^T, dP = dO V^T, then dV^T += dO^T (P_hi + P_lo) and
-//    dK^T += Q^T (dS_hi + dS_lo), each operand split into two BF16 terms
-//    and accumulated hi then lo.  Keys of the masked text range get exact
-//    zeros.
-// All MFMAs are v_mfma_f32_32x32x16_bf16; transposed operands are written to
-// LDS with the reduction index permuted (bits 2 and 3 of the index in each
-// 16-chunk swapped) to match the accumulator layout of the probabilities.
+//    stored for the key-side passes.  Then over the key tiles in the
+//    forward's logical order: S^T = K Q^T, dP^T = V dO^T,
+//    P = exp2(s*c - LSE*log2 e), dS = P (dP - D), dQ^T += K^T dS^T with dS
+//    split into two BF16 terms (hi = bf16(dS), lo = bf16(dS - hi))
+//    accumulated hi then lo.
+//  * dK and dV passes (key-tile-major): per wave 32 keys held in registers.
+//    Query tiles of 64 rows are visited in a frozen logical order -- valid
+//    text rows from 0, image rows from T_txt, then padded text rows from
+//    L_b -- so the sum over queries of a key never depends on the batch or
+//    the launch.  S = Q K^T and, for dK, dP = dO V^T; then
+//    dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), each
+//    accumulated hi then lo.  Keys of the masked text range get exact zeros.
+// All MFMAs are v_mfma_f32_32x32x16_bf16.  Per accumulator the order is:
+// scores and dP over the 8 head-dim chunks in order; gradients over the
+// 16-row chunks of the streamed side in its frozen order, hi then lo.
+//
+// Schedule (bit-neutral): every pass runs 8-wave workgroups, waves w and
+// w+4 on one SIMD; group 0 (waves 0-3) and group 1 (waves 4-7) alternate,
+// one barrier per phase, between a matrix phase (the gradient MFMAs of tile
+// t, then the scores -- and dP -- of tile t+1) and a VALU phase (P, dS and
+// the hi/lo split for tile t+1).  Streamed tiles are triple-buffered in LDS
+// and filled by direct global->LDS loads issued in the VALU phase two tiles
+// ahead; transposed operands come from ds_read_b64_tr_b16 on row-major
+// tiles (see qi_lds.h).
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_lds.h"
@@ -34,33 +43,12 @@ namespace qi {
 
 namespace {
 
-constexpr int kRow = 272;    // bytes per row-major 128-channel row in LDS
-constexpr int kTRow = 144;   // bytes per transposed row (64 entries + pad)
+using namespace lds;
+static_assert(kTileRows == kBwdBN && kTileRows == kBwdBM, "backward tiles are LDS tiles");
+
 constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);  // log2(e)/sqrt(128)
 constexpr float kLog2e = 1.4426950408889634074f;
 constexpr float kScale = (float)(1.0 / 11.313708498984760390);  // 1/sqrt(128)
-
-__device__ __forceinline__ int swap23(int a4) {  // position of key 4*a4 (a4 = 0..15)
-  return 16 * (a4 >> 2) + 8 * (a4 & 1) + 4 * ((a4 >> 1) & 1);
-}
-
-// 4 consecutive rows x 8 channels of a [rows,128] tile -> row-major LDS and
-// transposed (permuted) LDS.
-__device__ __forceinline__ void store_rows_and_t(char* rm, char* tr, const u32x4* x, int a4, int c16) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) *(u32x4*)(rm + (4 * a4 + r) * kRow + c16 * 16) = x[r];
-  if (tr) {
-    const int pos = swap23(a4);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x0 = x[0][w], x1 = x[1][w], x2 = x[2][w], x3 = x[3][w];
-      u32x2 lo = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-      u32x2 hi = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-      *(u32x2*)(tr + (8 * c16 + 2 * w) * kTRow + pos * 2) = lo;
-      *(u32x2*)(tr + (8 * c16 + 2 * w + 1) * kTRow + pos * 2) = hi;
-    }
-  }
-}
 
 __device__ __forceinline__ void split_pack(const float* v, uint32_t* hi, uint32_t* lo) {
   // v[0..7] -> hi[0..3], lo[0..3] packed BF16 pairs
@@ -72,11 +60,6 @@ __device__ __forceinline__ void split_pack(const float* v, uint32_t* hi, uint32_
     const float r1 = v[2 * w + 1] - bf16_hi(h);
     lo[w] = pack_bf16x2(r0, r1);
   }
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t* w) {
-  const u32x4 v = {w[0], w[1], w[2], w[3]};
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ void decode_bh(const BwdArgs& a, int ntiles, int& b, int& h, int& tile) {
@@ -95,28 +78,133 @@ __device__ __forceinline__ void decode_bh(const BwdArgs& a, int ntiles, int& b, 
   h = bh - b * a.H;
 }
 
-// ----------------------------------------------------------------- dQ pass
-// Workgroup = 8 waves x 32 query rows of one (b, h); waves w and w+4 share a
-// SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) alternate, one barrier
-// per phase, between a matrix phase (dQ^T += K_t^T dS_t^T with dS split
-// hi/lo, then the scores and dP of tile t+1: 64 MFMAs) and a VALU phase
-// (P, dS and its split for tile t+1).  K and V tiles are triple-buffered in
-// LDS (96 KiB) and filled by direct loads: in its VALU phase of tile t group
-// 0 loads V_{t+2} and group 1 K_{t+2}; each waits for its loads at the end
-// of its next matrix phase.  The arithmetic is the frozen one of the pass
-// (per accumulator: scores and dP over the 8 head-dim chunks in order, dQ
-// over the 16-key chunks in key order, hi then lo).
-using namespace lds;
-static_assert(kTileRows == kBwdBN, "dQ key tile is one LDS tile");
+// One direct global -> LDS load of one dword per lane: lane l's 4 bytes land
+// at LDS byte lds + 4*l (same M0 contract as dma16).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const char* base, uint32_t off32, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(off32), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-struct DqState {
-  f32x16 acc[4];       // dQ^T: 4 head-dim blocks x 32 queries
-  f32x16 s[2], dp[2];  // S^T and dP^T of one tile (two 32-key blocks)
-  u32x4 dh[4], dl[4];  // hi / lo BF16 dS^T of the four 16-key chunks
-  bf16x8 q[8], o[8];   // Q and dO rows of the wave's 32 queries
-  float lse2, D;
+// ------------------------------------------------------ matrix phase (all passes)
+// State of one wave: 32 rows of the fixed side (queries for dQ, keys for dK
+// and dV) in registers, one tile of the streamed side in LDS.
+struct GState {
+  f32x16 acc[4];        // gradient^T: 4 head-dim blocks x 32 fixed rows
+  f32x16 s[2], dp[2];   // scores and dP of one tile (two 32-row blocks)
+  u32x4 dh[4], dl[4];   // hi / lo BF16 B operand of the gradient, four 16-row chunks
+  bf16x8 b1[8], b2[8];  // fixed-side rows: B operands of the scores (b1) and dP (b2)
+  float lse2, D;        // dQ pass: LSE*log2 e and D of the lane's query
+};
+struct GBases {
+  uint32_t t, r1, r2;  // transposed tile (gradient), row tiles of the scores and of dP
+};
+// Steps: gradient steps j = 0..7 (chunk j/2, head-dim blocks 2(j%2) and
+// 2(j%2)+1; two transposed fragments, 4 MFMAs), then score steps: with dP,
+// j = 0..15 covers head-dim chunk j/2 of 32-row block j%2 (S and dP, two
+// row fragments); without, j = 0..7 covers chunk j of both blocks (S only).
+// Each step reads two fragments, kAhead steps before its MFMAs.
+constexpr int kAhead = 2;
+using Ring = bf16x8[kAhead + 1][2];
+
+template <bool kAcc, bool kS, bool kDp>
+struct Plan {
+  static constexpr int nacc = kAcc ? 8 : 0;
+  static constexpr int n = nacc + (kS ? (kDp ? 16 : 8) : 0);
+  static constexpr int reads(int k) { return k < n ? (k < nacc ? 4 : 2) : 0; }
+  static constexpr int later(int k) {  // LDS reads issued after step k's own, before its MFMAs
+    int r = 0;
+    for (int i = 1; i <= kAhead; ++i) r += reads(k + i);
+    return r;
+  }
 };
 
+template <bool kAcc, bool kS, bool kDp, int k>
+__device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
+  using P = Plan<kAcc, kS, kDp>;
+  if constexpr (k < P::n) {
+    bf16x8* x = f[k % (kAhead + 1)];
+    if constexpr (k < P::nacc) {
+      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
+      x[0] = tr_frag<c2, d0>(b.t);
+      x[1] = tr_frag<c2, d1>(b.t);
+    } else if constexpr (kDp) {
+      constexpr int j = k - P::nacc, kk = j >> 1, kb = j & 1;
+      x[0] = row_frag<kk, kb>(b.r1);
+      x[1] = row_frag<kk, kb>(b.r2);
+    } else {
+      constexpr int kk = k - P::nacc;
+      x[0] = row_frag<kk, 0>(b.r1);
+      x[1] = row_frag<kk, 1>(b.r1);
+    }
+  }
+}
+
+template <bool kAcc, bool kS, bool kDp, int k>
+__device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
+  using P = Plan<kAcc, kS, kDp>;
+  if constexpr (k < P::n) {
+    g_issue<kAcc, kS, kDp, k + kAhead>(f, b);
+    constexpr int later = P::later(k);
+    bf16x8* x = f[k % (kAhead + 1)];
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
+    if constexpr (k < P::nacc) {
+      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
+      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d0]);
+      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d1]);
+      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d0]);
+      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
+    } else if constexpr (kDp) {
+      constexpr int j = k - P::nacc, kk = j >> 1, kb = j & 1;
+      st.s[kb] = mfma32(x[0], st.b1[kk], st.s[kb]);
+      st.dp[kb] = mfma32(x[1], st.b2[kk], st.dp[kb]);
+    } else {
+      constexpr int kk = k - P::nacc;
+      st.s[0] = mfma32(x[0], st.b1[kk], st.s[0]);
+      st.s[1] = mfma32(x[1], st.b1[kk], st.s[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    g_step<kAcc, kS, kDp, k + 1>(st, f, b);
+  }
+}
+
+template <bool kAcc, bool kS, bool kDp, int k>
+__device__ __forceinline__ void g_prefetch(Ring& f, const GBases& b) {
+  if constexpr (k < kAhead) {
+    g_issue<kAcc, kS, kDp, k>(f, b);
+    g_prefetch<kAcc, kS, kDp, k + 1>(f, b);
+  }
+}
+
+template <bool kAcc, bool kS, bool kDp>
+__device__ __forceinline__ void g_matrix(GState& st, GBases b) {
+  if (kS) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st.s[kb][r] = 0.f;
+        if (kDp) st.dp[kb][r] = 0.f;
+      }
+  }
+  Ring f;
+  // opaque copies keep the per-step address XORs inside their steps
+  asm volatile("" : "+v"(b.t), "+v"(b.r1), "+v"(b.r2));
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  g_prefetch<kAcc, kS, kDp, 0>(f, b);
+  __builtin_amdgcn_sched_barrier(0);
+  g_step<kAcc, kS, kDp, 0>(st, f, b);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// ----------------------------------------------------------------- dQ pass
+// Key tiles in the forward's logical order.  Group 0 loads V_{t+2} and
+// group 1 K_{t+2} in their VALU phase of tile t.
 __device__ __forceinline__ void dq_bounds(int t, int ntxt, int L, int T_txt, int T_img, int& key0, int& nvalid) {
   if (t < ntxt) {
     key0 = t * kBwdBN;
@@ -130,7 +218,7 @@ __device__ __forceinline__ void dq_bounds(int t, int ntxt, int L, int T_txt, int
 
 // P = exp2(s*c - LSE*log2 e) (0 for masked keys), dS = P (dP - D), split
 // into hi = bf16(dS), lo = bf16(dS - hi) per 16-key chunk.
-__device__ __forceinline__ void dq_softmax(DqState& st, int cur_valid, int hh) {
+__device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     float ds[16];
@@ -151,85 +239,6 @@ __device__ __forceinline__ void dq_softmax(DqState& st, int cur_valid, int hh) {
   }
 }
 
-// Matrix phase, 4 LDS reads and 4 MFMAs per step, fragments read one step
-// ahead.  dQ steps j = 0..7: chunk c2 = j/2, head-dim blocks 2(j%2) and
-// 2(j%2)+1 from the transposed K_t tile.  Score steps j = 0..7: head-dim
-// chunk kk = j of both 32-key blocks of S^T (K_{t+1}) and dP^T (V_{t+1}).
-struct DqBases {
-  uint32_t tk, rk, rv;  // K_t transposed, K_{t+1} rows, V_{t+1} rows
-};
-using Ring = bf16x8[2][4];
-
-template <bool kDq, int k>
-__device__ __forceinline__ void dq_issue(Ring& f, const DqBases& b) {
-  constexpr int nsteps = (kDq ? 8 : 0) + 8;
-  if constexpr (k < nsteps) {
-    bf16x8* x = f[k & 1];
-    if constexpr (kDq && k < 8) {
-      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
-      x[0] = tr_frag<c2, d0>(b.tk);
-      x[1] = tr_frag<c2, d1>(b.tk);
-    } else {
-      constexpr int kk = kDq ? k - 8 : k;
-      x[0] = row_frag<kk, 0>(b.rk);
-      x[1] = row_frag<kk, 0>(b.rv);
-      x[2] = row_frag<kk, 1>(b.rk);
-      x[3] = row_frag<kk, 1>(b.rv);
-    }
-  }
-}
-
-template <bool kDq, bool kS, int k>
-__device__ __forceinline__ void dq_step(DqState& st, Ring& f, const DqBases& b) {
-  constexpr int nsteps = (kDq ? 8 : 0) + (kS ? 8 : 0);
-  if constexpr (k < nsteps) {
-    if constexpr (!(kDq && !kS && k + 1 >= 8)) dq_issue<kDq, k + 1>(f, b);
-    // LDS reads issued after this step's: the next step's 4
-    constexpr int later = (k + 1 < nsteps) ? 4 : 0;
-    bf16x8* x = f[k & 1];
-    if constexpr (kDq && k < 8) {
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
-      constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
-      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d0]);
-      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d1]);
-      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d0]);
-      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "i"(later));
-      constexpr int kk = kDq ? k - 8 : k;
-      st.s[0] = mfma32(x[0], st.q[kk], st.s[0]);
-      st.dp[0] = mfma32(x[1], st.o[kk], st.dp[0]);
-      st.s[1] = mfma32(x[2], st.q[kk], st.s[1]);
-      st.dp[1] = mfma32(x[3], st.o[kk], st.dp[1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    dq_step<kDq, kS, k + 1>(st, f, b);
-  }
-}
-
-template <bool kDq, bool kS>
-__device__ __forceinline__ void dq_matrix(DqState& st, DqBases b) {
-  if (kS) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        st.s[kb][r] = 0.f;
-        st.dp[kb][r] = 0.f;
-      }
-  }
-  Ring f;
-  // opaque copies keep the per-step address XORs inside their steps
-  asm volatile("" : "+v"(b.tk), "+v"(b.rk), "+v"(b.rv));
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kDq)
-    dq_issue<true, 0>(f, b);
-  else
-    dq_issue<false, 0>(f, b);
-  __builtin_amdgcn_sched_barrier(0);
-  dq_step<kDq, kS, 0>(st, f, b);
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArgs a) {
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
   const int qrow = qt * (kBwdDqWaves * 32) + wave * 32 + lr;
   const bool qvalid = qrow < a.S;
 
-  DqState st;
+  GState st;
   float dpart = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -257,8 +266,8 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
       o0 = *(const f32x4*)orow;
       o1 = *(const f32x4*)(orow + 4);
     }
-    st.q[kk] = __builtin_bit_cast(bf16x8, zq);
-    st.o[kk] = __builtin_bit_cast(bf16x8, zd);
+    st.b1[kk] = __builtin_bit_cast(bf16x8, zq);
+    st.b2[kk] = __builtin_bit_cast(bf16x8, zd);
     // D_i = dO_i . O_i (FP32 pre-cast O), fixed order: chunk, then channel
     const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
@@ -304,10 +313,10 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
     load_rows(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
   };
   auto bases = [&](int t) {
-    DqBases bb;
-    bb.tk = tr_base(addr_of(kbuf(t)), lane);
-    bb.rk = row_base(addr_of(kbuf(t + 1)), lane);
-    bb.rv = row_base(addr_of(vbuf(t + 1)), lane);
+    GBases bb;
+    bb.t = tr_base(addr_of(kbuf(t)), lane);
+    bb.r1 = row_base(addr_of(kbuf(t + 1)), lane);
+    bb.r2 = row_base(addr_of(vbuf(t + 1)), lane);
     return bb;
   };
 
@@ -326,13 +335,11 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
   // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
   if (grp == 1) bar();
   {
-    DqBases b0;
-    b0.tk = 0;
-    b0.rk = row_base(addr_of(kbuf(0)), lane);
-    b0.rv = row_base(addr_of(vbuf(0)), lane);
-    __builtin_amdgcn_s_setprio(1);
-    dq_matrix<false, true>(st, b0);
-    __builtin_amdgcn_s_setprio(0);
+    GBases b0;
+    b0.t = 0;
+    b0.r1 = row_base(addr_of(kbuf(0)), lane);
+    b0.r2 = row_base(addr_of(vbuf(0)), lane);
+    g_matrix<false, true, true>(st, b0);
   }
   bar();
   for (int t = 0; t + 1 < nt; ++t) {
@@ -344,22 +351,18 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
     }
     dq_softmax(st, valid_of(t), hh);
     bar();
-    __builtin_amdgcn_s_setprio(1);
-    dq_matrix<true, true>(st, bases(t));
-    __builtin_amdgcn_s_setprio(0);
+    g_matrix<true, true, true>(st, bases(t));
     __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
     bar();
   }
   dq_softmax(st, valid_of(nt - 1), hh);
   bar();
   {
-    DqBases bl;
-    bl.tk = tr_base(addr_of(kbuf(nt - 1)), lane);
-    bl.rk = 0;
-    bl.rv = 0;
-    __builtin_amdgcn_s_setprio(1);
-    dq_matrix<true, false>(st, bl);
-    __builtin_amdgcn_s_setprio(0);
+    GBases bl;
+    bl.t = tr_base(addr_of(kbuf(nt - 1)), lane);
+    bl.r1 = 0;
+    bl.r2 = 0;
+    g_matrix<true, false, true>(st, bl);
   }
   if (grp == 0) bar();
 
@@ -376,188 +379,230 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
   }
 }
 
-// --------------------------------------------------------------- dK/dV pass
+// ------------------------------------------------------------ dK and dV passes
 namespace {
-constexpr int kKQ = kBwdBM * kRow;       // Q row-major
-constexpr int kKDO = kBwdBM * kRow;      // dO row-major
-constexpr int kKQT = kHeadDim * kTRow;   // Q^T
-constexpr int kKDOT = kHeadDim * kTRow;  // dO^T
-constexpr int kKBuf = kKQ + kKDO + kKQT + kKDOT + 2 * kBwdBM * 4;  // + lse2, D
-constexpr int kKeysPerWG = 128;
-}  // namespace
 
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kKBuf];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Query tiles in the frozen order: valid text, image, padded text.
+struct QTiles {
+  int L, T_txt, T_img, nq_txt, nq_img, nq_pad;
+  __device__ QTiles(int L_, int T_txt_, int T_img_) : L(L_), T_txt(T_txt_), T_img(T_img_) {
+    nq_txt = (L + kBwdBM - 1) / kBwdBM;
+    nq_img = (T_img + kBwdBM - 1) / kBwdBM;
+    nq_pad = (T_txt - L + kBwdBM - 1) / kBwdBM;
+  }
+  __device__ int count() const { return nq_txt + nq_img + nq_pad; }
+  __device__ void bounds(int t, int& q0, int& nq) const {
+    if (t < nq_txt) {
+      q0 = t * kBwdBM;
+      nq = min(kBwdBM, L - q0);
+    } else if (t < nq_txt + nq_img) {
+      const int ti = t - nq_txt;
+      q0 = T_txt + ti * kBwdBM;
+      nq = min(kBwdBM, T_img - ti * kBwdBM);
+    } else {
+      const int ti = t - nq_txt - nq_img;
+      q0 = L + ti * kBwdBM;
+      nq = min(kBwdBM, T_txt - L - ti * kBwdBM);
+    }
+  }
+};
+
+// P = exp2(s*c - LSE*log2 e) and, for dK, dS = P (dP - D), per query row
+// (register r of block qb holds query 32*qb + 8*(r/4) + 4*hh + r%4); rows
+// past the tile's valid count are exactly 0.  Split hi/lo per 16-row chunk.
+template <bool kDk>
+__device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const float* dd, int nq, int hh) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q0 = 32 * qb + 8 * j + 4 * hh;
+      const f32x4 lv = *(const f32x4*)(lse + q0);
+      f32x4 dv = {0.f, 0.f, 0.f, 0.f};
+      if (kDk) dv = *(const f32x4*)(dd + q0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * j + u;
+        const bool valid = q0 + u < nq;
+        const float l2 = lv[u] * kLog2e;
+        const float p = valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[qb][r], kC, -l2)) : 0.f;
+        x[r] = kDk ? (valid ? p * (st.dp[qb][r] - dv[u]) : 0.f) : p;
+      }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t hi[4], lo[4];
+      split_pack(x + 8 * half, hi, lo);
+      st.dh[2 * qb + half] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      st.dl[2 * qb + half] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+  }
+}
+
+constexpr int kKvKeysPerWG = kBwdKvWaves * 32;
+constexpr int kKvSmem = 6 * kTileB + 2 * 3 * kBwdBM * 4;  // Q[3], dO[3] tiles; LSE[3], D[3] rows
+
+// kDk: dK pass (S, dP, dK^T += Q^T dS); else dV pass (S, dV^T += dO^T P).
+// Loads two tiles ahead in the VALU phase of tile t -- dK: group 0 dO and D,
+// group 1 Q and LSE; dV: group 0 Q and LSE, group 1 dO -- each group waiting
+// for its loads at the end of its next matrix phase.
+template <bool kDk>
+__device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, sub = wave & 3;
   const int lr = lane & 31, hh = lane >> 5;
   int b, h, kt;
   decode_bh(a, a.n_ktiles, b, h, kt);
   const int L = a.txt_len[b];
-  const int nkt_txt = (L + kKeysPerWG - 1) / kKeysPerWG;
-  const int nkt_img = (a.T_img + kKeysPerWG - 1) / kKeysPerWG;
-  const int nkt_pad = (a.T_txt - L + kKeysPerWG - 1) / kKeysPerWG;
+  const int nkt_txt = (L + kKvKeysPerWG - 1) / kKvKeysPerWG;
+  const int nkt_img = (a.T_img + kKvKeysPerWG - 1) / kKvKeysPerWG;
+  const int nkt_pad = (a.T_txt - L + kKvKeysPerWG - 1) / kKvKeysPerWG;
   if (kt >= nkt_txt + nkt_img + nkt_pad) return;  // whole workgroup
 
   int kbase, kend;
   bool zero_only = false;
-  if (kt < nkt_txt) { kbase = kt * kKeysPerWG; kend = L; }
-  else if (kt < nkt_txt + nkt_img) { kbase = a.T_txt + (kt - nkt_txt) * kKeysPerWG; kend = a.S; }
-  else { kbase = L + (kt - nkt_txt - nkt_img) * kKeysPerWG; kend = a.T_txt; zero_only = true; }
+  if (kt < nkt_txt) {
+    kbase = kt * kKvKeysPerWG;
+    kend = L;
+  } else if (kt < nkt_txt + nkt_img) {
+    kbase = a.T_txt + (kt - nkt_txt) * kKvKeysPerWG;
+    kend = a.S;
+  } else {
+    kbase = L + (kt - nkt_txt - nkt_img) * kKvKeysPerWG;
+    kend = a.T_txt;
+    zero_only = true;
+  }
   const int key = kbase + 32 * wave + lr;
   const bool kvalid = key < kend;
+  float* const out = kvalid ? (kDk ? a.dk.row(b, key, h) : a.dv.row(b, key, h)) : nullptr;
 
-  if (zero_only) {
+  if (zero_only) {  // masked text keys: exact zeros (whole workgroup)
     if (kvalid) {
-      float* dkr = a.dk.row(b, key, h);
-      float* dvr = a.dv.row(b, key, h);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        *(f32x4*)(dkr + 64 * hh + 4 * i) = z;
-        *(f32x4*)(dvr + 64 * hh + 4 * i) = z;
-      }
+      for (int i = 0; i < 16; ++i) *(f32x4*)(out + 64 * hh + 4 * i) = z;
     }
-    return;  // whole workgroup takes this branch
+    return;
   }
 
-  bf16x8 kreg[8], vreg[8];
+  GState st;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
     if (kvalid) {
       zk = *(const u32x4*)(a.k.row(b, key, h) + 16 * kk + 8 * hh);
-      zv = *(const u32x4*)(a.v.row(b, key, h) + 16 * kk + 8 * hh);
+      if (kDk) zv = *(const u32x4*)(a.v.row(b, key, h) + 16 * kk + 8 * hh);
     }
-    kreg[kk] = __builtin_bit_cast(bf16x8, zk);
-    vreg[kk] = __builtin_bit_cast(bf16x8, zv);
+    st.b1[kk] = __builtin_bit_cast(bf16x8, zk);
+    st.b2[kk] = __builtin_bit_cast(bf16x8, zv);
   }
-
-  // frozen query order: valid text, image, padded text; tiles of 64 rows
-  const int nq_txt = (L + kBwdBM - 1) / kBwdBM;
-  const int nq_img = (a.T_img + kBwdBM - 1) / kBwdBM;
-  const int nq_pad = (a.T_txt - L + kBwdBM - 1) / kBwdBM;
-  const int nqt = nq_txt + nq_img + nq_pad;
-  auto bounds = [&](int t, int& q0, int& nq) {
-    if (t < nq_txt) { q0 = t * kBwdBM; nq = min(kBwdBM, L - q0); }
-    else if (t < nq_txt + nq_img) { const int ti = t - nq_txt; q0 = a.T_txt + ti * kBwdBM; nq = min(kBwdBM, a.T_img - ti * kBwdBM); }
-    else { const int ti = t - nq_txt - nq_img; q0 = L + ti * kBwdBM; nq = min(kBwdBM, a.T_txt - L - ti * kBwdBM); }
-  };
-
-  f32x16 adk[4], adv[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { adk[d][r] = 0.f; adv[d][r] = 0.f; }
+    for (int r = 0; r < 16; ++r) st.acc[d][r] = 0.f;
 
-  const int tid = threadIdx.x, a4 = tid >> 4, c16 = tid & 15;
-  u32x4 qr[4], dr[4];
-  float l2v = INFINITY, dvv = 0.f;
-  const int64_t lbase = ((int64_t)b * a.H + h) * a.S;
-  auto load = [&](int q0, int nq) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qi = 4 * a4 + r;
-      u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
-      if (qi < nq) {
-        zq = *(const u32x4*)(a.q.row(b, q0 + qi, h) + 8 * c16);
-        zd = *(const u32x4*)(a.dO.row(b, q0 + qi, h) + 8 * c16);
-      }
-      qr[r] = zq;
-      dr[r] = zd;
-    }
-    l2v = INFINITY;
-    dvv = 0.f;
-    if (tid < kBwdBM && tid < nq) {
-      l2v = a.lse[lbase + q0 + tid] * kLog2e;
-      dvv = a.Dvec[lbase + q0 + tid];
-    }
+  const QTiles qt(L, a.T_txt, a.T_img);
+  const int nt = qt.count();
+  char* const qbase = smem;
+  char* const obase = smem + 3 * kTileB;
+  float* const lbase = (float*)(smem + 6 * kTileB);
+  float* const dbase = lbase + 3 * kBwdBM;
+  auto qbuf = [&](int j) { return qbase + (j % 3) * kTileB; };
+  auto obuf = [&](int j) { return obase + (j % 3) * kTileB; };
+  auto lrow = [&](int j) { return lbase + (j % 3) * kBwdBM; };
+  auto drow = [&](int j) { return dbase + (j % 3) * kBwdBM; };
+  auto nq_of = [&](int j) {
+    int q0, nq;
+    qt.bounds(j, q0, nq);
+    return nq;
   };
-  auto store = [&](char* buf) {
-    store_rows_and_t(buf, buf + kKQ + kKDO, qr, a4, c16);
-    store_rows_and_t(buf + kKQ, buf + kKQ + kKDO + kKQT, dr, a4, c16);
-    if (tid < kBwdBM) {
-      float* f = (float*)(buf + kKQ + kKDO + kKQT + kKDOT);
-      f[tid] = l2v;
-      f[kBwdBM + tid] = dvv;
-    }
+  // each group loads only one of Q and dO: group 0 dO (dK) or Q (dV)
+  const bool loads_o = (grp == 0) == kDk;
+  const RowOff ro = row_offsets(loads_o ? a.dO.ss : a.q.ss, lane);
+  const int64_t hb = ((int64_t)b * a.H + h) * a.S;  // [b, h] row of LSE and D
+  auto load_q = [&](int j) {
+    int q0, nq;
+    qt.bounds(j, q0, nq);
+    load_rows(a.q, ro, qbuf(j), b, h, q0, nq, sub, lane);
+    if (sub == 0 && lane < nq) dma4((const char*)(a.lse + hb + q0), 4u * lane, addr_of((const char*)lrow(j)));
+  };
+  auto load_o = [&](int j) {
+    int q0, nq;
+    qt.bounds(j, q0, nq);
+    load_rows(a.dO, ro, obuf(j), b, h, q0, nq, sub, lane);
+    if (kDk && sub == 0 && lane < nq) dma4((const char*)(a.Dvec + hb + q0), 4u * lane, addr_of((const char*)drow(j)));
+  };
+  auto load_tile = [&](int j) {
+    if (loads_o)
+      load_o(j);
+    else
+      load_q(j);
+  };
+  auto bases = [&](int t, bool next) {
+    GBases bb;
+    bb.t = tr_base(addr_of(kDk ? qbuf(t) : obuf(t)), lane);
+    bb.r1 = next ? row_base(addr_of(qbuf(t + 1)), lane) : 0;
+    bb.r2 = next ? row_base(addr_of(obuf(t + 1)), lane) : 0;
+    return bb;
   };
 
-  int q0, nq;
-  bounds(0, q0, nq);
-  load(q0, nq);
-  store(smem);
-  __syncthreads();
-  for (int t = 0; t < nqt; ++t) {
-    const char* buf = smem + (t & 1) * kKBuf;
-    if (t + 1 < nqt) {
-      bounds(t + 1, q0, nq);
-      load(q0, nq);
-    }
-    const float* l2s = (const float*)(buf + kKQ + kKDO + kKQT + kKDOT);
-    const float* Ds = l2s + kBwdBM;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[qb][r] = 0.f; dp[qb][r] = 0.f; }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int off = (32 * qb + lr) * kRow + (16 * kk + 8 * hh) * 2;
-        s[qb] = mfma32(*(const bf16x8*)(buf + off), kreg[kk], s[qb]);
-        dp[qb] = mfma32(*(const bf16x8*)(buf + kKQ + off), vreg[kk], dp[qb]);
-      }
-    // lane <-> key; register r of block qb <-> query 32qb + 8(r/4) + 4hh + r%4
-    uint32_t phi[2][8], plo[2][8], hi[2][8], lo[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float p[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], kC, -l2s[qi]));
-        ds[r] = p[r] * (dp[qb][r] - Ds[qi]);
-      }
-      split_pack(p, phi[qb], plo[qb]);
-      split_pack(p + 8, phi[qb] + 4, plo[qb] + 4);
-      split_pack(ds, hi[qb], lo[qb]);
-      split_pack(ds + 8, hi[qb] + 4, lo[qb] + 4);
-    }
-    const char* qt_ = buf + kKQ + kKDO;
-    const char* dot_ = qt_ + kKQT;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int qb = c >> 1, half = c & 1;
-      const bf16x8 ph_ = as_bf16x8(phi[qb] + 4 * half), pl_ = as_bf16x8(plo[qb] + 4 * half);
-      const bf16x8 bh_ = as_bf16x8(hi[qb] + 4 * half), bl_ = as_bf16x8(lo[qb] + 4 * half);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int off = (32 * d + lr) * kTRow + (16 * c + 8 * hh) * 2;
-        const bf16x8 da = *(const bf16x8*)(dot_ + off);
-        adv[d] = mfma32(da, ph_, adv[d]);
-        adv[d] = mfma32(da, pl_, adv[d]);
-        const bf16x8 qa = *(const bf16x8*)(qt_ + off);
-        adk[d] = mfma32(qa, bh_, adk[d]);
-        adk[d] = mfma32(qa, bl_, adk[d]);
-      }
-    }
-    if (t + 1 < nqt) store(smem + ((t + 1) & 1) * kKBuf);
-    __syncthreads();
+  load_tile(0);
+  if (nt > 1) load_tile(1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  bar();
+
+  // Both groups run the same sequence; group 1 starts one barrier later, so
+  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
+  if (grp == 1) bar();
+  {
+    GBases b0;
+    b0.t = 0;
+    b0.r1 = row_base(addr_of(qbuf(0)), lane);
+    b0.r2 = row_base(addr_of(obuf(0)), lane);
+    g_matrix<false, true, kDk>(st, b0);
   }
+  bar();
+  for (int t = 0; t + 1 < nt; ++t) {
+    if (t + 2 < nt) load_tile(t + 2);
+    kv_softmax<kDk>(st, lrow(t), drow(t), nq_of(t), hh);
+    bar();
+    g_matrix<true, true, kDk>(st, bases(t, true));
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
+    bar();
+  }
+  kv_softmax<kDk>(st, lrow(nt - 1), drow(nt - 1), nq_of(nt - 1), hh);
+  bar();
+  g_matrix<true, false, kDk>(st, bases(nt - 1, false));
+  if (grp == 0) bar();
+
   if (kvalid) {
-    float* dkr = a.dk.row(b, key, h);
-    float* dvr = a.dv.row(b, key, h);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        *(f32x4*)(dvr + d0) = f32x4{adv[d][4 * g4], adv[d][4 * g4 + 1], adv[d][4 * g4 + 2], adv[d][4 * g4 + 3]};
-        *(f32x4*)(dkr + d0) = f32x4{adk[d][4 * g4] * kScale, adk[d][4 * g4 + 1] * kScale,
-                                    adk[d][4 * g4 + 2] * kScale, adk[d][4 * g4 + 3] * kScale};
+        if (kDk)
+          *(f32x4*)(out + d0) = f32x4{st.acc[d][4 * g4] * kScale, st.acc[d][4 * g4 + 1] * kScale,
+                                      st.acc[d][4 * g4 + 2] * kScale, st.acc[d][4 * g4 + 3] * kScale};
+        else
+          *(f32x4*)(out + d0) = f32x4{st.acc[d][4 * g4], st.acc[d][4 * g4 + 1], st.acc[d][4 * g4 + 2],
+                                      st.acc[d][4 * g4 + 3]};
       }
   }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dk_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
+  kv_pass<true>(a, smem);
+}
+
+__global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
+  kv_pass<false>(a, smem);
 }
 
 }  // namespace qi

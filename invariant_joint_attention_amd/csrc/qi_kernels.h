@@ -59,6 +59,7 @@ struct FwdArgs {
 constexpr int kBwdBN = 64;  // key tile of the dQ pass (= forward order)
 constexpr int kBwdBM = 64;  // query tile of the dK/dV pass (frozen)
 constexpr int kBwdDqWaves = 8;  // dQ pass: waves per workgroup (two alternating groups of 4)
+constexpr int kBwdKvWaves = 8;  // dK and dV passes: waves (x 32 keys) per workgroup
 
 struct BwdArgs {
   View<const uint16_t> q, k, v, dO;
@@ -77,6 +78,7 @@ __global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
 __global__ void dgain_fold_kernel(DgainFoldArgs a);
 __global__ void attn_fwd_kernel(FwdArgs a);
 __global__ void attn_bwd_dq_kernel(BwdArgs a);
-__global__ void attn_bwd_dkdv_kernel(BwdArgs a);
+__global__ void attn_bwd_dk_kernel(BwdArgs a);
+__global__ void attn_bwd_dv_kernel(BwdArgs a);
 
 }  // namespace qi
