@@ -160,6 +160,8 @@ size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
  *                  per-sample values summed in ascending b.
  *   workspace      device buffer of at least qi_joint_attn_bwd_workspace()
  *                  bytes, 256-byte aligned; its contents are scratch.
+ * The sequence strides of q, k, v and d_o must stay below 2^26 elements
+ * (QI_E_UNSUPPORTED otherwise), as in qi_joint_attn_fwd.
  */
 int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd q,
                       qi_bshd k, qi_bshd v, qi_bshd o_f32, const float* lse, qi_bshd d_o,

@@ -333,10 +333,10 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
   if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
   if ((rc = check_alias(ext))) return rc;
-  if ((rc = current_device_gate())) return rc;
-
   if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride))
     return fail(QI_E_UNSUPPORTED, "k/v sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if ((rc = current_device_gate())) return rc;
+
   const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
@@ -401,13 +401,13 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, Lw.total);
   ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + Lw.total, true});
   if ((rc = check_alias(ext))) return rc;
+  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride || q.ss > kFwdMaxRowStride ||
+                d_o.ss > kFwdMaxRowStride))
+    return fail(QI_E_UNSUPPORTED, "q/k/v/d_o sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
 
   char* ws = (char*)workspace;
   float* Dvec = (float*)(ws + Lw.dvec);
-  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride || q.ss > kFwdMaxRowStride ||
-                d_o.ss > kFwdMaxRowStride))
-    return fail(QI_E_UNSUPPORTED, "q/k/v/d_o sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   const int rows_per_wg = kBwdDqWaves * 32;
   const int keys_per_wg = kBwdKvWaves * 32;
   int nk_max = 0;

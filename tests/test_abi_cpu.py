@@ -159,3 +159,33 @@ def test_prologue_and_backward_validation():
 
 def test_strict_probe_without_gpu():
     assert qi.lib().qi_strict_probe(0) == code("QI_E_UNSUPPORTED")
+
+
+def test_row_strides_beyond_32_bit_lane_offsets_are_refused():
+    """The attention kernels address 16 rows of K, V (and Q, dO in the
+    backward) from one scalar base with 32-bit lane offsets; a sequence
+    stride of 2^26 elements or more is refused before any device work."""
+    g = geom()
+    big = (1 << 26) + 128
+    rc = fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, ss=big, sb=g.S * big))
+    assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error()
+    rc = fwd_call(g, v=fake_bshd(region(2), g.B, g.S, g.H, ss=big, sb=g.S * big))
+    assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error()
+    # at the limit itself the call passes validation (and stops at the device gate)
+    ok = 1 << 26
+    rc = fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, ss=ok, sb=g.S * ok))
+    assert rc == code("QI_E_UNSUPPORTED") and "stride" not in qi.last_error()
+
+    L = qi.lib()
+    ws = L.qi_joint_attn_bwd_workspace(g.ptr())
+    for bad in (0, 3):  # q_raw is not addressed by the attention passes; q and d_o are
+        views = [fake_bshd(region(i), g.B, g.S, g.H) for i in range(6)]
+        dout = fake_bshd(region(7), g.B, g.S, g.H)
+        if bad == 0:
+            dout = fake_bshd(region(7), g.B, g.S, g.H, ss=big, sb=g.S * big)
+        else:
+            views[2] = fake_bshd(region(2), g.B, g.S, g.H, ss=big, sb=g.S * big)  # q
+        grads = [fake_bshd(region(10 + i), g.B, g.S, g.H) for i in range(3)]
+        rc = L.qi_joint_attn_bwd(g.ptr(), *views, region(6), dout, region(8), region(9), *grads,
+                                 region(14), region(15), None, None, region(20), ws, None)
+        assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error(), qi.last_error()
