@@ -90,6 +90,7 @@ def main():
     o = torch.empty(shp, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((wl.B, wl.H, wl.S), dtype=torch.float32, device=dev)
     of = torch.empty(shp, dtype=torch.float32, device=dev) if wl.backward else None
+    fws = torch.empty(qi.fwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
     if wl.backward:
         ws = torch.empty(qi.bwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
         grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
@@ -104,7 +105,7 @@ def main():
         qi.qknorm_rope(g["k"], g["g_k"], geo, out=kp)
         if timed:
             e[1].record()
-        qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of)
+        qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of, workspace=fws)
         if timed:
             e[2].record()
         if wl.backward:

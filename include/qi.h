@@ -105,6 +105,10 @@ typedef struct {
 int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
                    float* y_f32, hipStream_t stream);
 
+/* Bytes of device workspace qi_joint_attn_fwd needs for this geometry
+ * (B*H*S*128 FP16 values, rounded up to 256 bytes); 0 for an invalid one. */
+size_t qi_joint_attn_fwd_workspace(const qi_geom* geom);
+
 /*
  * qi_joint_attn_fwd -- masked non-causal attention over [text, image].
  *   [Kernel list] rows joint_attn_qk_gemm, joint_attn_softmax,
@@ -120,15 +124,23 @@ int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
  *   lse      FP32 dense [B,H,S] output (kept for the backward).
  *   o_f32    nullable FP32 dense [B,S,H,128] output of the pre-cast O; the
  *            backward needs it.
- * P enters the A.V product as two BF16 terms (hi = bf16(p), lo = bf16(p-hi))
- * so the output meets 1e-2*|ref| + 2e-3 even where O cancels on a few
- * peaked keys; the row sum uses the FP32 p.
- * The sequence stride of k and v must stay below 2^26 elements (the kernel
+ *   workspace  device buffer of at least qi_joint_attn_fwd_workspace()
+ *            bytes, 256-byte aligned, not overlapping any other argument;
+ *            its contents are scratch (the call writes V there as FP16).
+ * The A.V product takes P and V in FP16: P rounded once (RNE), V as
+ * v * 2^-8 rounded once, which is exact for 2^-6 <= |v| <= 65504 * 2^8
+ * and keeps an absolute error below 2^-17 for smaller |v|; larger |v|
+ * (and non-finite v) give non-finite outputs.  A single BF16 rounding of P
+ * would break 1e-2*|ref| + 2e-3 where O cancels on a few peaked keys.
+ * The row sum uses the FP32 p.
+ * The sequence stride of k must stay below 2^26 elements (the kernel
  * addresses 16 key rows from one base with 32-bit offsets); larger strides
- * return QI_E_UNSUPPORTED.
+ * return QI_E_UNSUPPORTED.  A null, misaligned or short workspace returns
+ * QI_E_WORKSPACE / QI_E_ALIGN before any launch.
  */
 int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o,
-                      float* lse, float* o_f32, hipStream_t stream);
+                      float* lse, float* o_f32, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* Bytes of device workspace qi_joint_attn_bwd needs for this geometry. */
 size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
@@ -161,7 +173,7 @@ size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
  *   workspace      device buffer of at least qi_joint_attn_bwd_workspace()
  *                  bytes, 256-byte aligned; its contents are scratch.
  * The sequence strides of q, k, v and d_o must stay below 2^26 elements
- * (QI_E_UNSUPPORTED otherwise), as in qi_joint_attn_fwd.
+ * (QI_E_UNSUPPORTED otherwise).
  */
 int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd q,
                       qi_bshd k, qi_bshd v, qi_bshd o_f32, const float* lse, qi_bshd d_o,

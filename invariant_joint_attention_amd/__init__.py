@@ -22,7 +22,8 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
           5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
 
 # every entry point declared in include/qi.h
-SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_bwd_workspace", "qi_joint_attn_bwd",
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_bwd_workspace",
+           "qi_joint_attn_bwd",
            "qi_last_error", "qi_strict_probe", "qi_trace")
 
 
@@ -56,7 +57,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, G, S = ctypes.c_void_p, ctypes.POINTER(QiGeom), ctypes.c_void_p
         L.qi_qknorm_rope.argtypes = [G, QiBshd, P, QiBshd, P, S]
-        L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, S]
+        L.qi_joint_attn_fwd_workspace.argtypes = [G]
+        L.qi_joint_attn_fwd_workspace.restype = ctypes.c_size_t
+        L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_bwd_workspace.argtypes = [G]
         L.qi_joint_attn_bwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_bwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, P, QiBshd, P, P,
@@ -127,14 +130,23 @@ def qknorm_rope(x, gain, geom: Geometry, out=None, out_f32=None):
     return out
 
 
-def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None):
-    """Masked joint attention forward; returns (O BF16 [B,S,H,128], LSE FP32 [B,H,S])."""
+def fwd_workspace_bytes(geom: Geometry) -> int:
+    return int(lib().qi_joint_attn_fwd_workspace(geom.ptr()))
+
+
+def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None, workspace=None):
+    """Masked joint attention forward; returns (O BF16 [B,S,H,128], LSE FP32 [B,H,S]).
+    ``workspace`` is a device byte tensor of at least ``fwd_workspace_bytes``
+    (allocated here when omitted)."""
     if out is None:
         out = _empty(q.shape, torch.bfloat16, q)
     if lse is None:
         lse = _empty((geom.B, geom.H, geom.S), torch.float32, q)
+    if workspace is None:
+        workspace = _empty((max(1, fwd_workspace_bytes(geom)),), torch.uint8, q)
     _check(lib().qi_joint_attn_fwd(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
-                                   _ptr(out_f32), _stream()))
+                                   _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream()))
     return out, lse
 
 

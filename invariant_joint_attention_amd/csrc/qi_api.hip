@@ -223,6 +223,11 @@ struct BwdLayout {
   int n_txt_chunks, n_chunks;
 };
 
+// Forward workspace: V as FP16 (v * 2^-8), dense [B,H,S,128].
+size_t fwd_workspace_bytes(const qi_geom* g) {
+  return align256((size_t)g->B * g->H * seq_len(g) * kHeadDim * 2);
+}
+
 BwdLayout bwd_layout(const qi_geom* g) {
   BwdLayout L;
   const int64_t S = seq_len(g);
@@ -319,8 +324,13 @@ int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
   return launch_prologue(geom, x, gain, y, y_f32, stream);
 }
 
+size_t qi_joint_attn_fwd_workspace(const qi_geom* geom) {
+  if (check_geom(geom)) return 0;
+  return fwd_workspace_bytes(geom);
+}
+
 int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o, float* lse,
-                      float* o_f32, hipStream_t stream) {
+                      float* o_f32, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = check_geom(geom);
   if (rc) return rc;
   std::vector<Extent> ext;
@@ -332,18 +342,28 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
   if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
   if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  const size_t ws_need = fwd_workspace_bytes(geom);
+  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < ws_need)
+    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
+  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
   if ((rc = check_alias(ext))) return rc;
-  if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride))
-    return fail(QI_E_UNSUPPORTED, "k/v sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
 
+  uint16_t* v16 = (uint16_t*)workspace;  // FP16 V * 2^-8, dense [B,H,S,128]
   const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
     FwdArgs a;
     a.q = view_of<const uint16_t>(q, b0);
     a.k = view_of<const uint16_t>(k, b0);
-    a.v = view_of<const uint16_t>(v, b0);
+    a.v.p = v16 + (int64_t)b0 * geom->H * S * kHeadDim;
+    a.v.sb = (int64_t)geom->H * S * kHeadDim;
+    a.v.ss = kHeadDim;
+    a.v.sh = S * kHeadDim;
     a.o = view_of<uint16_t>(o, b0);
     a.lse = lse + (int64_t)b0 * geom->H * S;
     a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
@@ -355,6 +375,18 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
     a.n_qtiles = (int)ceil_div(S, rows_per_wg);
     a.xcd_remap = ((nb * geom->H) % 8) == 0;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+
+    VcastArgs c;
+    c.v = view_of<const uint16_t>(v, b0);
+    c.out = const_cast<uint16_t*>(a.v.p);
+    c.S = (int)S;
+    c.H = geom->H;
+    c.T_txt = geom->T_txt;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
+    const int64_t cast_blocks = ceil_div(S * geom->H * 16, 256);
+    hipLaunchKernelGGL(v_f16_kernel, dim3((unsigned)cast_blocks, nb), dim3(256), 0, stream, c);
+    if ((rc = launched("v_f16_kernel"))) return rc;
+
     const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
     hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
     if ((rc = launched("attn_fwd_kernel"))) return rc;
@@ -458,17 +490,17 @@ const char* qi_trace(void) {
   static const std::string s = [] {
     char buf[4096];
     snprintf(buf, sizeof buf,
-             "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":1,"
+             "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_cast\":\"v_f16_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
              "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
-             "\"mfma\":\"v_mfma_f32_32x32x16_bf16\",\"accumulator\":\"fp32\","
+             "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","
              "\"frozen\":{\"fwd_key_tile\":%d,\"bwd_dq_key_tile\":%d,\"bwd_dkdv_query_tile\":%d,"
              "\"prologue_dgain_chunk\":%d,\"key_order\":\"text tiles from 0, image tiles from T_txt\","
              "\"bwd_query_order\":\"valid text, image, padded text\","
              "\"softmax\":\"exp2(fma(s,log2e/sqrt(128),-m*c)); l sums fp32 P in register order\","
-             "\"fwd_p_split\":\"hi=bf16(P), lo=bf16(P-hi), accumulated hi then lo\","
+             "\"fwd_pv_operands\":\"P fp16 RNE, V fp16 RNE of v*2^-8, O=acc/(l*2^-8)\","
              "\"bwd_D\":\"rowsum(dO*O) from the fp32 forward O\","
              "\"reference_max_threshold_log2\":8,"
              "\"ds_split\":\"hi=bf16(dS), lo=bf16(dS-hi), accumulated hi then lo (dQ, dK)\","

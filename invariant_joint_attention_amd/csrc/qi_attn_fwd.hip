@@ -14,14 +14,18 @@
 //    the row max is an in-lane max plus one exchange with lane l^32, and the
 //    softmax rescale factor is a per-lane scalar.  Each 32-key block
 //    accumulates its 8 head-dim chunks in order.
-//  * O^T = V^T P^T accumulates in 4 blocks of 32x32 FP32.  P enters the MFMA
-//    as two BF16 terms, hi = bf16(p) and lo = bf16(p - hi), accumulated hi
-//    then lo for each 16-key chunk in key order: one BF16 rounding of P
-//    alone would move O by up to 2^-9 * sum_j p_j|v_j|, which breaks the
-//    output tolerance where O cancels on few, peaked keys.  The MFMA
-//    reduction index is a permutation of the 16 keys of a chunk (bits 2 and
-//    3 of the key index swapped) that matches the accumulator layout of P;
-//    the transposing V reads fetch the keys in that order.
+//  * O^T = V^T P^T accumulates in 4 blocks of 32x32 FP32 with
+//    v_mfma_f32_32x32x16_f16, one product per 16-key chunk in key order.
+//    P enters as FP16 (RNE; p <= 256, and values below 2^-24 that flush to
+//    zero weigh less than 2^-24 of a row whose largest p is at least 1), V
+//    as FP16 of v * 2^-8, written by a conversion pass over the valid keys
+//    (exact for 2^-6 <= |v| <= 65504 * 2^8; smaller |v| keep an absolute
+//    error below 2^-17).  One BF16 rounding of P would move O by up to
+//    2^-9 * sum_j p_j|v_j| / l, which breaks the output tolerance where O
+//    cancels on few, peaked keys; FP16 P has 2^-12.  The MFMA reduction index
+//    is a permutation of the 16 keys of a chunk (bits 2 and 3 of the key
+//    index swapped) that matches the accumulator layout of P; the
+//    transposing V reads fetch the keys in that order.
 //  * Keys are tiled LOGICALLY: ceil(L_b/64) text tiles starting at key 0,
 //    then ceil(T_img/64) image tiles starting at key T_txt.  Masked keys are
 //    never read (their LDS slots are zero) and get probability exactly 0, so
@@ -30,7 +34,8 @@
 //  * Online softmax in the exp2 domain with c = log2(e)/sqrt(128):
 //    p = exp2(s*c - m*c) (one fma); the row sum l adds the FP32 p lane by lane
 //    in register order, then the two half-waves (commutative, so both get the
-//    same bits); O = acc / l and LSE = (m*c + log2 l) * ln 2.
+//    same bits); O = acc / (l * 2^-8) (exact rescaling of the V scale) and
+//    LSE = (m*c + log2 l) * ln 2.
 //    The reference max m moves only when a tile max exceeds it by more than
 //    8/c (so p <= 256): each lane decides from its own row alone, and the
 //    rescale (factor exactly 1 where m did not move) is skipped when no lane
@@ -39,7 +44,7 @@
 // Schedule (free; does not change any bit):
 //  * Workgroup = 8 waves x 32 query rows of one (b, h).  Waves w and w+4 run
 //    on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) alternate
-//    between a matrix phase (P*V of tile t plus the scores of tile t+1, 48
+//    between a matrix phase (P*V of tile t plus the scores of tile t+1, 32
 //    MFMAs) and a softmax phase (VALU only), one workgroup barrier per phase,
 //    so each SIMD has one wave issuing MFMAs while its partner runs the
 //    softmax.  Group 1 starts one barrier later; both run 2*nt + 1 barriers.
@@ -55,6 +60,8 @@
 //    (vmcnt) at the end of its next matrix phase, a barrier before the tile
 //    is read.  Three buffers are needed because group 0's softmax phase runs
 //    while group 1 still reads the tiles of tile t-1.
+//  * The softmax phase ends with P rounded to FP16, so one FP32 score buffer
+//    suffices: the matrix phase accumulates the next tile's scores into it.
 //  * The matrix phase issues its LDS reads as inline asm two steps ahead of
 //    use and waits for each step's reads with an exact lgkmcnt; the direct
 //    loads are inline asm too, so the compiler neither inserts waits for
@@ -74,6 +81,19 @@ static_assert(kTileRows == kFwdBN, "forward key tile is one LDS tile");
 // log2(e) / sqrt(128), rounded once to FP32
 constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);
 constexpr float kLn2 = 0.69314718055994530942f;
+// V enters P*V as FP16 of v * 2^-8; the epilogue divides by l * 2^-8.
+constexpr float kVScale = 0x1p-8f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two FP32 values -> packed FP16 pair (lo = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 // Threshold on raw scores for moving the reference max: 8 in the exp2 domain.
 constexpr float kTauRaw = (float)(8.0 / (1.4426950408889634074 / 11.313708498984760390));
 
@@ -89,37 +109,51 @@ __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, i
   }
 }
 
-// Per-lane LDS bases of the matrix phase: K row fragments (scores) and V
-// transposed fragments (P*V).
+// Per-lane LDS addresses of the matrix phase, relative to K buffer 0 and V
+// buffer 0: eight K row-fragment bases (one per 16-channel chunk kk) and
+// eight V transposed-read bases (one per 32-channel block d and half r).
+// The 32-key block and the 16-key chunk go into the reads' immediate
+// offsets and each matrix phase adds its buffers' offsets; the XOR patterns
+// touch address bits 5-7 only, below the 1 KiB-aligned buffer starts, so
+// base ^ pattern + offset is exact.
 struct Addr {
-  uint32_t ak, av;
+  uint32_t k[8], v[8];
 };
 __device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
   Addr a;
-  a.ak = row_base(lds0, lane);
-  a.av = tr_base(lds0 + 3 * kTileB, lane);
+  const uint32_t rb = row_base(lds0, lane), tb = tr_base(lds0 + 3 * kTileB, lane);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) a.k[kk] = rb ^ (uint32_t)(kk << 5);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a.v[i] = tb ^ (uint32_t)((i >> 1) << 6) ^ (uint32_t)((i & 1) << 5);
+  // opaque: the compiler keeps the sixteen addresses instead of
+  // re-deriving them with VALU work inside the loop
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a.k[i]), "+v"(a.v[i]));
   return a;
 }
 
-// K fragment of score step k (block kb = k/8, kk = k%8): block 0 is finished
-// in the first half of the matrix phase and block 1 is started in the
-// second, when the first two P chunks are no longer live.
+// K fragment of score step k (block kb = k/8, chunk kk = k%8).
 template <int k>
 __device__ __forceinline__ bf16x8 kfrag(const Addr& ad) {
   constexpr int kk = k & 7, kb = k >> 3;
-  return lds::row_frag<kk, kb>(ad.ak);
+  return __builtin_bit_cast(bf16x8, ds_b128<kb * 32 * kRowB>(ad.k[kk]));
 }
-// V^T fragment of P*V step k (c2 = k/4, d = k%4).
+// V^T fragment of P*V step k (16-key chunk c2 = k/4, 32-channel block d = k%4).
 template <int k>
-__device__ __forceinline__ bf16x8 vfrag(const Addr& ad) {
+__device__ __forceinline__ f16x8 vfrag(const Addr& ad) {
   constexpr int c2 = k >> 2, d = k & 3;
-  return lds::tr_frag<c2, d>(ad.av);
+  constexpr int o = c2 * 16 * kRowB;
+  const u32x2v r0 = ds_tr<o>(ad.v[2 * d]);
+  const u32x2v r1 = ds_tr<o + 8 * kRowB>(ad.v[2 * d + 1]);
+  const u32x4 v = {r0.x, r0.y, r1.x, r1.y};
+  return __builtin_bit_cast(f16x8, v);
 }
 
 struct State {
   f32x16 acc[4];
-  f32x16 s[2][2];      // two score / P buffers (tile parity), two 32-key blocks each
-  u32x4 ph[2], pl[2];  // hi/lo BF16 P of two 16-key chunks (chunk parity)
+  f32x16 s[2];   // scores of one 64-key tile (two 32-key blocks), FP32
+  u32x4 ph[4];   // FP16 P of the tile's four 16-key chunks
   bf16x8 q[8];
   float m_used, l_lane;
 };
@@ -129,34 +163,19 @@ __device__ __forceinline__ void s_only(State& st, const char* kbuf, int lane) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.s[0][kb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int kk = k >> 1, kb = k & 1;
     const bf16x8 kv = *(const bf16x8*)(kbuf + off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
-    st.s[0][kb] = mfma32(kv, st.q[kk], st.s[0][kb]);
+    st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
   }
 }
 
-// hi/lo BF16 split of 16-key chunk c2 of the P in buffer X, into slot c2 % 2.
-template <int X, int c2>
-__device__ __forceinline__ void pack_chunk(State& st) {
-  constexpr int kb = c2 >> 1, r0 = 8 * (c2 & 1);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float p0 = st.s[X][kb][r0 + 2 * w], p1 = st.s[X][kb][r0 + 2 * w + 1];
-    const uint32_t u = pack_bf16x2(p0, p1);
-    st.ph[c2 & 1][w] = u;
-    st.pl[c2 & 1][w] = pack_bf16x2(p0 - bf16_lo(u), p1 - bf16_hi(u));
-  }
-}
-
-// Softmax of one tile (scores in buffer X, replaced by P in place): mask, row
-// max, lazy reference-max move, p = exp2, row sum; then the hi/lo split of
-// the first 16-key chunk (the matrix phase splits the others one chunk ahead).
-template <int X>
+// Softmax of one tile: mask, row max, lazy reference-max move, p = exp2, row
+// sum; then P rounded to FP16 (RNE) for the P*V products.
 __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
-  f32x16 (&sx)[2] = st.s[X];
+  f32x16 (&sx)[2] = st.s;
   if (cur_valid < kFwdBN) {
     // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
     const int lim = cur_valid - 4 * hh;
@@ -193,72 +212,82 @@ __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
       ts = ts + sx[kb][r];
     }
   st.l_lane = st.l_lane + ts;
-  pack_chunk<X, 0>(st);
+#pragma unroll
+  for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int kb = c2 >> 1, r = 8 * (c2 & 1) + 2 * w;
+      st.ph[c2][w] = pack_f16x2(sx[kb][r], sx[kb][r + 1]);
+    }
 }
 
-// Matrix phase: O^T += V^T P_hi^T then V^T P_lo^T per 16-key chunk, and,
-// when kS, S^T of the next tile interleaved (one score MFMA between the hi
-// and lo products).  Step k's fragments are read kPre steps ahead; sched
-// barriers pin that order and each step waits only for its own reads.
+// Matrix phase: O^T += V^T P^T per 16-key chunk and, when kS, S^T of the
+// next tile interleaved (16 + 16 MFMAs).  Step k's fragments are read kPre
+// steps ahead; sched barriers pin that order and each step waits only for
+// its own reads.  The first score MFMA of each 32-key block starts from a
+// zero accumulator.
 constexpr int kPre = 2;
 
 template <bool kS, int k>
-__device__ __forceinline__ void mm_issue(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+__device__ __forceinline__ void mm_issue(f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
   if constexpr (k < 16) {
     vr[k % (kPre + 1)] = vfrag<k>(ad);
     if constexpr (kS) kr[k % (kPre + 1)] = kfrag<k>(ad);
   }
 }
 
-template <bool kS, int X, int k>
-__device__ __forceinline__ void mm_step(State& st, bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+template <bool kS, int k>
+__device__ __forceinline__ void mm_step(State& st, f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
   if constexpr (k < 16) {
     mm_issue<kS, k + kPre>(vr, kr, ad);
     // reads issued after step k's own: those of steps k+1 .. k+kPre
     constexpr int per = kS ? 3 : 2;
     constexpr int ahead = (15 - k) < kPre ? (15 - k) : kPre;
     constexpr int later = per * ahead;
-    bf16x8& vv = vr[k % (kPre + 1)];
+    f16x8& vv = vr[k % (kPre + 1)];
     bf16x8& kv = kr[k % (kPre + 1)];
     if constexpr (kS)
       asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vv), "+v"(kv) : "i"(later));
     else
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vv) : "i"(later));
     constexpr int c2 = k >> 2, d = k & 3;
-    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.ph[c2 & 1]), st.acc[d]);
-    if constexpr (kS) st.s[1 - X][k >> 3] = mfma32(kv, st.q[k & 7], st.s[1 - X][k >> 3]);
-    st.acc[d] = mfma32(vv, __builtin_bit_cast(bf16x8, st.pl[c2 & 1]), st.acc[d]);
-    // split the next chunk while this chunk's products run
-    if constexpr ((k & 3) == 1 && c2 < 3) pack_chunk<X, c2 + 1>(st);
+    st.acc[d] = mfma32h(vv, __builtin_bit_cast(f16x8, st.ph[c2]), st.acc[d]);
+    if constexpr (kS) {
+      constexpr int kb = k >> 3, kk = k & 7;
+      if constexpr (kk == 0)
+        st.s[kb] = mfma32(kv, st.q[kk], f32x16{});
+      else
+        st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    mm_step<kS, X, k + 1>(st, vr, kr, ad);
+    mm_step<kS, k + 1>(st, vr, kr, ad);
   }
 }
 
 template <bool kS, int k>
-__device__ __forceinline__ void mm_prefetch(bf16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
+__device__ __forceinline__ void mm_prefetch(f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
   if constexpr (k < kPre) {
     mm_issue<kS, k>(vr, kr, ad);
     mm_prefetch<kS, k + 1>(vr, kr, ad);
   }
 }
 
-template <bool kS, int X>
-__device__ __forceinline__ void mm_tile(State& st, const Addr& ad) {
-  if (kS) {
+// Matrix phase of tile t: V_t in V buffer t % 3, K_{t+1} in K buffer
+// (t + 1) % 3; kofs / vofs are those buffers' byte offsets (wave-uniform).
+template <bool kS>
+__device__ __forceinline__ void mm_tile(State& st, const Addr& ad, uint32_t kofs, uint32_t vofs) {
+  Addr a2;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.s[1 - X][kb][r] = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    a2.k[i] = ad.k[i] + kofs;
+    a2.v[i] = ad.v[i] + vofs;
   }
-  bf16x8 vr[kPre + 1], kr[kPre + 1];
-  // opaque copies: keeps the per-step address XORs inside their steps
-  Addr a2 = ad;
-  asm volatile("" : "+v"(a2.ak), "+v"(a2.av));
+  f16x8 vr[kPre + 1];
+  bf16x8 kr[kPre + 1];
   __builtin_amdgcn_sched_barrier(0);
   mm_prefetch<kS, 0>(vr, kr, a2);
   __builtin_amdgcn_sched_barrier(0);
-  mm_step<kS, X, 0>(st, vr, kr, a2);
+  mm_step<kS, 0>(st, vr, kr, a2);
 }
 
 }  // namespace
@@ -335,43 +364,21 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   bar();
 
   const Addr ad = make_addr((uint32_t)(uintptr_t)(lds_char*)smem, lane);
-  // matrix phase of tile t: V_t in vbuf[t % 3], K_{t+1} in kbuf[(t + 1) % 3];
-  // P of tile t in score buffer t & 1, scores of tile t+1 into the other
-  auto mm = [&](int t, auto par, auto ks) {
-    constexpr int X = decltype(par)::value;
-    constexpr bool S = decltype(ks)::value;
-    Addr a2;
-    a2.av = ad.av + (t % 3) * kTileB;
-    a2.ak = ad.ak + ((t + 1) % 3) * kTileB;
-    __builtin_amdgcn_s_setprio(1);
-    mm_tile<S, X>(st, a2);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  using Yes = std::true_type;
-  using No = std::false_type;
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
   // one tile with a successor: group 0 loads V_{t+1}, group 1 K_{t+2};
   // softmax; matrix phase; each group waits for its own loads
-  auto tile = [&](int t, auto par) {
-    constexpr int X = decltype(par)::value;
+  auto tile = [&](int t) {
     if (grp == 1) {
       if (t + 2 < nt) load_k(t + 2);
     } else {
       load_v(t + 1);
     }
-    softmax_tile<X>(st, valid_of(t), hh);
+    softmax_tile(st, valid_of(t), hh);
     bar();
-    mm(t, par, Yes{});
+    __builtin_amdgcn_s_setprio(1);
+    mm_tile<true>(st, ad, ((t + 1) % 3) * kTileB, (t % 3) * kTileB);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
     bar();
-  };
-  auto last = [&](int t, auto par) {
-    constexpr int X = decltype(par)::value;
-    softmax_tile<X>(st, valid_of(t), hh);
-    bar();
-    mm(t, par, No{});
-    if (grp == 0) bar();
   };
 
   // Both groups run the same sequence; group 1 starts one barrier later, so
@@ -381,20 +388,18 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   s_only(st, kbuf(0), lane);
   __builtin_amdgcn_s_setprio(0);
   bar();
-  int t = 0;
-  for (; t + 2 < nt; t += 2) {
-    tile(t, B0{});
-    tile(t + 1, B1{});
-  }
-  if (t + 1 < nt) {
-    tile(t, B0{});
-    last(t + 1, B1{});
-  } else {
-    last(t, B0{});
-  }
+  for (int t = 0; t + 1 < nt; ++t) tile(t);
+  softmax_tile(st, valid_of(nt - 1), hh);
+  bar();
+  __builtin_amdgcn_s_setprio(1);
+  mm_tile<false>(st, ad, 0, ((nt - 1) % 3) * kTileB);
+  __builtin_amdgcn_s_setprio(0);
+  if (grp == 0) bar();
 
   // ---- epilogue: O = acc / l, one RNE cast; LSE in natural log
   const float l_tot = st.l_lane + __shfl_xor(st.l_lane, 32);
+  // acc holds sum_j p_j v_j 2^-8: divide by l * 2^-8 (exact scaling)
+  const float l_div = l_tot * kVScale;
   if (qvalid) {
     uint16_t* orow = a.o.row(b, qrow, h);
     float* frow = a.of ? a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim : nullptr;
@@ -403,8 +408,8 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        const float o0 = st.acc[d][4 * g4] / l_tot, o1 = st.acc[d][4 * g4 + 1] / l_tot;
-        const float o2 = st.acc[d][4 * g4 + 2] / l_tot, o3 = st.acc[d][4 * g4 + 3] / l_tot;
+        const float o0 = st.acc[d][4 * g4] / l_div, o1 = st.acc[d][4 * g4 + 1] / l_div;
+        const float o2 = st.acc[d][4 * g4 + 2] / l_div, o3 = st.acc[d][4 * g4 + 3] / l_div;
         const u32x2 ov = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
         *(u32x2*)(orow + d0) = ov;
         if (frow) *(f32x4*)(frow + d0) = f32x4{o0, o1, o2, o3};
@@ -414,6 +419,26 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
       a.lse[((int64_t)b * a.H + h) * a.S + qrow] = lse2 * kLn2;
     }
   }
+}
+
+
+// V -> FP16 of v * 2^-8 into a dense [B, H, S, 128] buffer, for the rows of
+// valid keys (padded text keys are never read by the attention kernel).
+// One thread converts 8 channels; the multiply by 2^-8 is exact and the
+// FP16 conversion rounds to nearest even.
+__global__ __launch_bounds__(256) void v_f16_kernel(VcastArgs a) {
+  const int b = blockIdx.y;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int c = (int)(gid & 15);
+  const int64_t r = gid >> 4;  // j * H + h
+  if (r >= (int64_t)a.S * a.H) return;
+  const int j = (int)(r / a.H), h = (int)(r - (int64_t)j * a.H);
+  if (j >= a.txt_len[b] && j < a.T_txt) return;
+  const u32x4 w = *(const u32x4*)(a.v.row(b, j, h) + 8 * c);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_f16x2(bf16_lo(w[i]) * kVScale, bf16_hi(w[i]) * kVScale);
+  *(u32x4*)(a.out + (((int64_t)b * a.H + h) * a.S + j) * kHeadDim + 8 * c) = o;
 }
 
 }  // namespace qi

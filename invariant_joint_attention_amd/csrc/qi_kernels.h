@@ -77,6 +77,15 @@ __global__ void qknorm_rope_fwd_kernel(PrologueArgs a);
 __global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
 __global__ void dgain_fold_kernel(DgainFoldArgs a);
 __global__ void attn_fwd_kernel(FwdArgs a);
+
+// V -> FP16 (v * 2^-8) conversion pass of the forward.
+struct VcastArgs {
+  View<const uint16_t> v;  // BF16 [B,S,H,128] (B of this launch)
+  uint16_t* out;           // FP16 dense [B,H,S,128]
+  int S, H, T_txt;
+  int txt_len[kMaxBatchPerLaunch];
+};
+__global__ void v_f16_kernel(VcastArgs a);
 __global__ void attn_bwd_dq_kernel(BwdArgs a);
 __global__ void attn_bwd_dk_kernel(BwdArgs a);
 __global__ void attn_bwd_dv_kernel(BwdArgs a);

@@ -59,14 +59,17 @@ def region(i):
     return BASE + i * (1 << 32)
 
 
-def fwd_call(geom, q=None, k=None, v=None, o=None, lse=None, of=None):
+def fwd_call(geom, q=None, k=None, v=None, o=None, lse=None, of=None, ws=None, ws_bytes=None):
     g = geom
     q = q or fake_bshd(region(0), g.B, g.S, g.H)
     k = k or fake_bshd(region(1), g.B, g.S, g.H)
     v = v or fake_bshd(region(2), g.B, g.S, g.H)
     o = o or fake_bshd(region(3), g.B, g.S, g.H)
     lse = region(4) if lse is None else lse
-    return qi.lib().qi_joint_attn_fwd(g.ptr(), q, k, v, o, lse, of, None)
+    ws = region(5) if ws is None else ws
+    if ws_bytes is None:
+        ws_bytes = qi.lib().qi_joint_attn_fwd_workspace(g.ptr())
+    return qi.lib().qi_joint_attn_fwd(g.ptr(), q, k, v, o, lse, of, ws, ws_bytes, None)
 
 
 def geom(**kw):
@@ -95,9 +98,10 @@ def code(name):
 ])
 def test_invalid_geometry_fails_closed(kw, expect):
     g = geom(**kw)
-    assert fwd_call(g) == code(expect)
+    assert fwd_call(g, ws_bytes=1 << 20) == code(expect)
     assert qi.last_error() != ""
     assert qi.lib().qi_joint_attn_bwd_workspace(g.ptr()) == 0
+    assert qi.lib().qi_joint_attn_fwd_workspace(g.ptr()) == 0
 
 
 def test_null_and_misaligned_pointers():
@@ -108,6 +112,21 @@ def test_null_and_misaligned_pointers():
     # a stride that is not a multiple of 16 bytes
     assert fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, sh=132)) == code("QI_E_ALIGN")
     assert fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, sh=-128)) == code("QI_E_INVALID")
+
+
+def test_forward_workspace_validation():
+    g = geom()
+    L = qi.lib()
+    ws = L.qi_joint_attn_fwd_workspace(g.ptr())
+    # B*H*S*128 FP16 values, rounded up to 256 bytes
+    assert ws == -(-(g.B * g.H * g.S * 128 * 2) // 256) * 256
+    assert fwd_call(g, ws=0) == code("QI_E_WORKSPACE")
+    assert fwd_call(g, ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    assert fwd_call(g, ws=region(5) + 16) == code("QI_E_ALIGN")
+    # the workspace may overlap nothing else, inputs included
+    assert fwd_call(g, ws=region(2)) == code("QI_E_ALIAS")
+    assert fwd_call(g, ws=region(3) + 256) == code("QI_E_ALIAS")
+    assert fwd_call(g) == code("QI_E_UNSUPPORTED")  # valid: stops at the device gate
 
 
 def test_aliasing_is_rejected():
@@ -169,8 +188,9 @@ def test_row_strides_beyond_32_bit_lane_offsets_are_refused():
     big = (1 << 26) + 128
     rc = fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, ss=big, sb=g.S * big))
     assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error()
+    # v is read by a conversion pass with 64-bit addressing, so its stride is free
     rc = fwd_call(g, v=fake_bshd(region(2), g.B, g.S, g.H, ss=big, sb=g.S * big))
-    assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error()
+    assert rc == code("QI_E_UNSUPPORTED") and "stride" not in qi.last_error()
     # at the limit itself the call passes validation (and stops at the device gate)
     ok = 1 << 26
     rc = fwd_call(g, k=fake_bshd(region(1), g.B, g.S, g.H, ss=ok, sb=g.S * ok))

@@ -144,17 +144,32 @@ def test_forward_full_sampled(orc, cfg):
 
 
 def test_forward_constant_v_and_scaling():
+    """V enters A.V as FP16 of v * 2^-8, which is exact for BF16 values of
+    magnitude 2^-9 and above (multiples of 2^-16 after the scale); with such
+    a V the weights' exact normalisation returns a constant V bit for bit and
+    doubling V doubles O and leaves LSE alone.  Smaller |v| keep an absolute
+    error below 2^-17 before the output cast."""
     wl = small_wl(("c", 1, 2, 40, (29,), 9, 7), seed=5)
     inp, g = gpu_inputs(wl)
     geo = geom_of(wl)
     q = qi.qknorm_rope(g["q"], g["g_q"], geo)
     k = qi.qknorm_rope(g["k"], g["g_k"], geo)
-    vc = g["v"][:, :1].expand_as(g["v"]).contiguous()
+    tiny = g["v"].abs() < 2.0 ** -9
+    v = torch.where(tiny, torch.zeros_like(g["v"]), g["v"])
+    vc = v[:, :1].expand_as(v).contiguous()
     oc, _ = qi.joint_attn_fwd(q, k, vc, geo)
     assert torch.equal(oc, vc), "constant V must be returned exactly"
-    o1, l1 = qi.joint_attn_fwd(q, k, g["v"], geo)
-    o2, l2 = qi.joint_attn_fwd(q, k, (g["v"].float() * 2).to(torch.bfloat16), geo)
+    o1, l1 = qi.joint_attn_fwd(q, k, v, geo)
+    o2, l2 = qi.joint_attn_fwd(q, k, (v.float() * 2).to(torch.bfloat16), geo)
     assert torch.equal(o2, (o1.float() * 2).to(torch.bfloat16)) and torch.equal(l1, l2)
+    # large magnitudes (beyond FP16's own range, within the 2^-8 scale's)
+    o3, _ = qi.joint_attn_fwd(q, k, (v.float() * 2.0 ** 14).to(torch.bfloat16), geo)
+    assert torch.equal(o3, (o1.float() * 2.0 ** 14).to(torch.bfloat16))
+    # tiny magnitudes: a constant V of values below 2^-9 comes back within the FP16 quantum
+    vt = (g["v"][:, :1] * 2.0 ** -12).to(torch.bfloat16).expand_as(v).contiguous()
+    ot, _ = qi.joint_attn_fwd(q, k, vt, geo)
+    err = (ot.float() - vt.float()).abs().max().item()
+    assert err <= 2.0 ** -16, err
 
 
 # ------------------------------------------------------------------ backward
