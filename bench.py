@@ -9,7 +9,7 @@ backward (attention + prologue gradients).  Prints ONE JSON line.
 
 value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
 with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).
-The attention-forward call (the V-to-FP16 pass and the attention kernel,
+The attention-forward call (the V-to-FP16 tile pass and the attention kernel,
 launched back to back on one stream) is also timed alone with HIP events on
 the launch stream; that time gives the roofline fraction against the MI355X
 dense BF16 MFMA peak (2.5 PFLOP/s).  The CPU oracle is timed on a bounded
@@ -137,9 +137,9 @@ def main():
     attn_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     pro_bytes = 2 * 2 * 2 * wl.B * wl.S * wl.H * 128  # Q and K, read + write BF16
 
-    # one forward call = v_f16_kernel (V to FP16) + attn_fwd_kernel, timed together on the launch stream
+    # one forward call = v_tiles_kernel (V to FP16 key tiles) + attn_fwd_kernel, timed together on the launch stream
     traffic = traffic_from_profile("attn_fwd_call", "qi_attn_fwd.hip", args.workload)
-    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel (+ v_f16_kernel: one forward call)",
+    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel (+ v_tiles_kernel: one forward call)",
                 "achieved": round(attn_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "flops_per_launch": fwd_flops, "avg_launch_ms": round(fwd_ms, 4)}

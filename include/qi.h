@@ -105,8 +105,9 @@ typedef struct {
 int qi_qknorm_rope(const qi_geom* geom, qi_bshd x, const float* gain, qi_bshd y,
                    float* y_f32, hipStream_t stream);
 
-/* Bytes of device workspace qi_joint_attn_fwd needs for this geometry
- * (B*H*S*128 FP16 values, rounded up to 256 bytes); 0 for an invalid one. */
+/* Bytes of device workspace qi_joint_attn_fwd needs for this geometry:
+ * B*H*nt*64*128 FP16 values with nt = ceil(T_txt/64) + ceil(grid_h*grid_w/64)
+ * key tiles, rounded up to 256 bytes; 0 for an invalid geometry. */
 size_t qi_joint_attn_fwd_workspace(const qi_geom* geom);
 
 /*
@@ -126,7 +127,8 @@ size_t qi_joint_attn_fwd_workspace(const qi_geom* geom);
  *            backward needs it.
  *   workspace  device buffer of at least qi_joint_attn_fwd_workspace()
  *            bytes, 256-byte aligned, not overlapping any other argument;
- *            its contents are scratch (the call writes V there as FP16).
+ *            its contents are scratch (the call writes V there as FP16
+ *            transposed key tiles).
  * The A.V product takes P and V in FP16: P rounded once (RNE), V as
  * v * 2^-8 rounded once, which is exact for 2^-6 <= |v| <= 65504 * 2^8
  * and keeps an absolute error below 2^-17 for smaller |v|; larger |v|

@@ -223,9 +223,14 @@ struct BwdLayout {
   int n_txt_chunks, n_chunks;
 };
 
-// Forward workspace: V as FP16 (v * 2^-8), dense [B,H,S,128].
+// Forward workspace: V as FP16 (v * 2^-8) transposed key tiles [B][H][nt_max][128][64].
+// key tiles per (b, h) at the longest valid text: text tiles, then image tiles
+int fwd_nt_max(const qi_geom* g) {
+  return (int)(ceil_div(g->T_txt, kFwdBN) + ceil_div((int64_t)g->grid_h * g->grid_w, kFwdBN));
+}
+
 size_t fwd_workspace_bytes(const qi_geom* g) {
-  return align256((size_t)g->B * g->H * seq_len(g) * kHeadDim * 2);
+  return align256((size_t)g->B * g->H * fwd_nt_max(g) * kVtileElems * 2);
 }
 
 BwdLayout bwd_layout(const qi_geom* g) {
@@ -353,17 +358,15 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
     return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
 
-  uint16_t* v16 = (uint16_t*)workspace;  // FP16 V * 2^-8, dense [B,H,S,128]
+  uint16_t* vt = (uint16_t*)workspace;  // FP16 V^T key tiles [B][H][nt_max][128][64]
+  const int nt_max = fwd_nt_max(geom);
   const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
     FwdArgs a;
     a.q = view_of<const uint16_t>(q, b0);
     a.k = view_of<const uint16_t>(k, b0);
-    a.v.p = v16 + (int64_t)b0 * geom->H * S * kHeadDim;
-    a.v.sb = (int64_t)geom->H * S * kHeadDim;
-    a.v.ss = kHeadDim;
-    a.v.sh = S * kHeadDim;
+    a.vt = vt + (int64_t)b0 * geom->H * nt_max * kVtileElems;
     a.o = view_of<uint16_t>(o, b0);
     a.lse = lse + (int64_t)b0 * geom->H * S;
     a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
@@ -372,20 +375,22 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
     a.H = geom->H;
     a.T_txt = geom->T_txt;
     a.T_img = geom->grid_h * geom->grid_w;
+    a.nt_max = nt_max;
     a.n_qtiles = (int)ceil_div(S, rows_per_wg);
     a.xcd_remap = ((nb * geom->H) % 8) == 0;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
 
-    VcastArgs c;
+    VtileArgs c;
     c.v = view_of<const uint16_t>(v, b0);
-    c.out = const_cast<uint16_t*>(a.v.p);
-    c.S = (int)S;
+    c.out = const_cast<uint16_t*>(a.vt);
     c.H = geom->H;
     c.T_txt = geom->T_txt;
+    c.T_img = a.T_img;
+    c.nt_max = nt_max;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
-    const int64_t cast_blocks = ceil_div(S * geom->H * 16, 256);
-    hipLaunchKernelGGL(v_f16_kernel, dim3((unsigned)cast_blocks, nb), dim3(256), 0, stream, c);
-    if ((rc = launched("v_f16_kernel"))) return rc;
+    hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
+                       c);
+    if ((rc = launched("v_tiles_kernel"))) return rc;
 
     const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
     hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
@@ -492,7 +497,7 @@ const char* qi_trace(void) {
     snprintf(buf, sizeof buf,
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_cast\":\"v_f16_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
              "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","

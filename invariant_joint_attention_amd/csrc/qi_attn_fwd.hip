@@ -18,14 +18,14 @@
 //    v_mfma_f32_32x32x16_f16, one product per 16-key chunk in key order.
 //    P enters as FP16 (RNE; p <= 256, and values below 2^-24 that flush to
 //    zero weigh less than 2^-24 of a row whose largest p is at least 1), V
-//    as FP16 of v * 2^-8, written by a conversion pass over the valid keys
-//    (exact for 2^-6 <= |v| <= 65504 * 2^8; smaller |v| keep an absolute
+//    as FP16 of v * 2^-8, written by a conversion pass as transposed key
+//    tiles (exact for 2^-6 <= |v| <= 65504 * 2^8; smaller |v| keep an absolute
 //    error below 2^-17).  One BF16 rounding of P would move O by up to
 //    2^-9 * sum_j p_j|v_j| / l, which breaks the output tolerance where O
 //    cancels on few, peaked keys; FP16 P has 2^-12.  The MFMA reduction index
 //    is a permutation of the 16 keys of a chunk (bits 2 and 3 of the key
 //    index swapped) that matches the accumulator layout of P; the
-//    transposing V reads fetch the keys in that order.
+//    conversion pass stores the keys of each chunk in that order.
 //  * Keys are tiled LOGICALLY: ceil(L_b/64) text tiles starting at key 0,
 //    then ceil(T_img/64) image tiles starting at key T_txt.  Masked keys are
 //    never read (their LDS slots are zero) and get probability exactly 0, so
@@ -48,13 +48,13 @@
 //    MFMAs) and a softmax phase (VALU only), one workgroup barrier per phase,
 //    so each SIMD has one wave issuing MFMAs while its partner runs the
 //    softmax.  Group 1 starts one barrier later; both run 2*nt + 1 barriers.
-//  * LDS: K tiles in kbuf[j % 3], V tiles in vbuf[j % 3], 96 KiB.  Rows are
-//    unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key
-//    (swizzle bits 2-3 from key bits 0-1, bits 0-1 from key bits 2-3), so
-//    the K fragment reads (16 keys per 16-lane group), the transposing V
-//    reads (ds_read_b64_tr_b16, 4 keys x 4 chunks per 32-lane group, V
-//    stays row-major) and the contiguous direct-load writes meet no LDS bank
-//    conflict on the 64 banks.  Tiles are filled by direct global->LDS loads
+//  * LDS: K tiles in kbuf[j % 3], V^T tiles in vbuf[j % 3], 96 KiB.  K rows
+//    are unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key
+//    (swizzle bits 2-3 from key bits 0-1, bits 0-1 from key bits 2-3); V^T
+//    tiles are 128 channel lines of 128 bytes swizzled by channel/2.  The K
+//    and V^T fragment reads (one ds_read_b128 each, 16 rows per 16-lane
+//    group) and the contiguous direct-load writes meet no LDS bank conflict
+//    on the 64 banks.  Tiles are filled by direct global->LDS loads
 //    (global_load_lds_dwordx4) issued in the softmax phase of tile t: group
 //    0 loads V_{t+1}, group 1 loads K_{t+2}; each waits for its loads
 //    (vmcnt) at the end of its next matrix phase, a barrier before the tile
@@ -111,25 +111,27 @@ __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, i
 
 // Per-lane LDS addresses of the matrix phase, relative to K buffer 0 and V
 // buffer 0: eight K row-fragment bases (one per 16-channel chunk kk) and
-// eight V transposed-read bases (one per 32-channel block d and half r).
-// The 32-key block and the 16-key chunk go into the reads' immediate
-// offsets and each matrix phase adds its buffers' offsets; the XOR patterns
-// touch address bits 5-7 only, below the 1 KiB-aligned buffer starts, so
-// base ^ pattern + offset is exact.
+// four V^T fragment bases (one per 16-key chunk c2).  The 32-key block and
+// the 32-channel block go into the reads' immediate offsets and each matrix
+// phase adds its buffers' offsets; the XOR patterns touch address bits 5-7
+// only, below the 1 KiB-aligned buffer starts, so base ^ pattern + offset is
+// exact.
 struct Addr {
-  uint32_t k[8], v[8];
+  uint32_t k[8], v[4];
 };
 __device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
   Addr a;
-  const uint32_t rb = row_base(lds0, lane), tb = tr_base(lds0 + 3 * kTileB, lane);
+  const uint32_t rb = row_base(lds0, lane), tb = vt_base(lds0 + 3 * kTileB, lane);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) a.k[kk] = rb ^ (uint32_t)(kk << 5);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a.v[i] = tb ^ (uint32_t)((i >> 1) << 6) ^ (uint32_t)((i & 1) << 5);
-  // opaque: the compiler keeps the sixteen addresses instead of
+  for (int c2 = 0; c2 < 4; ++c2) a.v[c2] = tb ^ (uint32_t)(c2 << 5);
+  // opaque: the compiler keeps the twelve addresses instead of
   // re-deriving them with VALU work inside the loop
 #pragma unroll
-  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a.k[i]), "+v"(a.v[i]));
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a.k[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(a.v[i]));
   return a;
 }
 
@@ -139,15 +141,12 @@ __device__ __forceinline__ bf16x8 kfrag(const Addr& ad) {
   constexpr int kk = k & 7, kb = k >> 3;
   return __builtin_bit_cast(bf16x8, ds_b128<kb * 32 * kRowB>(ad.k[kk]));
 }
-// V^T fragment of P*V step k (16-key chunk c2 = k/4, 32-channel block d = k%4).
+// V^T fragment of P*V step k (16-key chunk c2 = k/4, 32-channel block d = k%4):
+// channel rows 32*d .. 32*d+31, one 16-byte read per lane.
 template <int k>
 __device__ __forceinline__ f16x8 vfrag(const Addr& ad) {
   constexpr int c2 = k >> 2, d = k & 3;
-  constexpr int o = c2 * 16 * kRowB;
-  const u32x2v r0 = ds_tr<o>(ad.v[2 * d]);
-  const u32x2v r1 = ds_tr<o + 8 * kRowB>(ad.v[2 * d + 1]);
-  const u32x4 v = {r0.x, r0.y, r1.x, r1.y};
-  return __builtin_bit_cast(f16x8, v);
+  return __builtin_bit_cast(f16x8, ds_b128<d * 32 * kVtRowB>(ad.v[c2]));
 }
 
 struct State {
@@ -241,7 +240,7 @@ __device__ __forceinline__ void mm_step(State& st, f16x8 (&vr)[kPre + 1], bf16x8
   if constexpr (k < 16) {
     mm_issue<kS, k + kPre>(vr, kr, ad);
     // reads issued after step k's own: those of steps k+1 .. k+kPre
-    constexpr int per = kS ? 3 : 2;
+    constexpr int per = kS ? 2 : 1;
     constexpr int ahead = (15 - k) < kPre ? (15 - k) : kPre;
     constexpr int later = per * ahead;
     f16x8& vv = vr[k % (kPre + 1)];
@@ -278,10 +277,9 @@ template <bool kS>
 __device__ __forceinline__ void mm_tile(State& st, const Addr& ad, uint32_t kofs, uint32_t vofs) {
   Addr a2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a2.k[i] = ad.k[i] + kofs;
-    a2.v[i] = ad.v[i] + vofs;
-  }
+  for (int i = 0; i < 8; ++i) a2.k[i] = ad.k[i] + kofs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a2.v[i] = ad.v[i] + vofs;
   f16x8 vr[kPre + 1];
   bf16x8 kr[kPre + 1];
   __builtin_amdgcn_sched_barrier(0);
@@ -341,17 +339,15 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
     tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
     return nv;
   };
-  const RowOff ko = row_offsets(a.k.ss, lane), vo = row_offsets(a.v.ss, lane);
+  const RowOff ko = row_offsets(a.k.ss, lane);
+  const VtOff vo = vt_offsets(lane);
+  const uint16_t* const vt_bh = a.vt + ((int64_t)b * a.H + h) * a.nt_max * kVtileElems;
   auto load_k = [&](int j) {
     int k0, nv;
     tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
     load_rows(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
   };
-  auto load_v = [&](int j) {
-    int k0, nv;
-    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
-    load_rows(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
-  };
+  auto load_v = [&](int j) { load_vt(vt_bh + (int64_t)j * kVtileElems, vo, vbuf(j), sub); };
 
   // prologue: K_0, V_0 (group 0) and K_1 (group 1)
   if (grp == 0) {
@@ -422,23 +418,44 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
 }
 
 
-// V -> FP16 of v * 2^-8 into a dense [B, H, S, 128] buffer, for the rows of
-// valid keys (padded text keys are never read by the attention kernel).
-// One thread converts 8 channels; the multiply by 2^-8 is exact and the
-// FP16 conversion rounds to nearest even.
-__global__ __launch_bounds__(256) void v_f16_kernel(VcastArgs a) {
-  const int b = blockIdx.y;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int c = (int)(gid & 15);
-  const int64_t r = gid >> 4;  // j * H + h
-  if (r >= (int64_t)a.S * a.H) return;
-  const int j = (int)(r / a.H), h = (int)(r - (int64_t)j * a.H);
-  if (j >= a.txt_len[b] && j < a.T_txt) return;
-  const u32x4 w = *(const u32x4*)(a.v.row(b, j, h) + 8 * c);
-  u32x4 o;
+// V -> FP16 V^T key tiles.  One workgroup per (logical key tile t, h, b):
+// the tile's valid key rows are staged in LDS as BF16, then written out as
+// 128 channel rows of 64 FP16 values v * 2^-8 (the multiply is exact, the
+// conversion rounds to nearest even), the keys of each 16-key chunk in the
+// A.V reduction order (position p holds key p with bits 2 and 3 swapped).
+// Keys past the tile's valid count are written as zero, so the attention
+// kernel loads whole tiles and a masked key's V slot is exactly zero.
+__global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {
+  __shared__ uint32_t tl[kFwdBN][kHeadDim / 2 + 1];  // [key][channel pair]; one pad word per row
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = a.txt_len[b];
+  const int ntxt = (L + kFwdBN - 1) / kFwdBN;
+  const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
+  if (t >= nt) return;
+  int key0, nvalid;
+  tile_bounds(t, ntxt, L, a.T_txt, a.T_img, key0, nvalid);
+  for (int i = threadIdx.x; i < kFwdBN * 16; i += 256) {
+    const int key = i >> 4, c = i & 15;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (key < nvalid) w = *(const u32x4*)(a.v.row(b, key0 + key, h) + 8 * c);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_f16x2(bf16_lo(w[i]) * kVScale, bf16_hi(w[i]) * kVScale);
-  *(u32x4*)(a.out + (((int64_t)b * a.H + h) * a.S + j) * kHeadDim + 8 * c) = o;
+    for (int e = 0; e < 4; ++e) tl[key][4 * c + e] = w[e];
+  }
+  __syncthreads();
+  uint16_t* const out = a.out + (((int64_t)b * a.H + h) * a.nt_max + t) * kVtileElems;
+  for (int i = threadIdx.x; i < kHeadDim * 8; i += 256) {
+    const int d = i >> 3, j = i & 7;  // channel row, 8-key chunk of the row
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = 8 * (j & 1) + e;  // position within 16-key chunk j/2
+      const int key = 16 * (j >> 1) + ((p & 3) | (((p >> 3) & 1) << 2) | (((p >> 2) & 1) << 3));
+      const uint32_t w = tl[key][d >> 1];
+      f[e] = ((d & 1) ? bf16_hi(w) : bf16_lo(w)) * kVScale;
+    }
+    const u32x4 o = {pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7])};
+    *(u32x4*)(out + d * kFwdBN + 8 * j) = o;
+  }
 }
 
 }  // namespace qi

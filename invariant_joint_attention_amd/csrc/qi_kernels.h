@@ -45,11 +45,13 @@ constexpr int kFwdRowsPerWave = 32;
 constexpr int64_t kFwdMaxRowStride = int64_t(1) << 26;
 
 struct FwdArgs {
-  View<const uint16_t> q, k, v;
+  View<const uint16_t> q, k;
+  const uint16_t* vt;  // FP16 V^T key tiles [B][H][nt_max][128][64] (B of this launch)
   View<uint16_t> o;
   float* lse;  // dense [B,H,S] (B of this launch)
   float* of;   // nullable dense [B,S,H,128]
   int B, S, H, T_txt, T_img;
+  int nt_max;     // key tiles per (b, h) slot of vt
   int n_qtiles;   // ceil(S / rows per workgroup)
   int xcd_remap;  // 1: group the query tiles of a (b, h) on one XCD
   int txt_len[kMaxBatchPerLaunch];
@@ -78,14 +80,18 @@ __global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
 __global__ void dgain_fold_kernel(DgainFoldArgs a);
 __global__ void attn_fwd_kernel(FwdArgs a);
 
-// V -> FP16 (v * 2^-8) conversion pass of the forward.
-struct VcastArgs {
+// V -> FP16 (v * 2^-8) conversion pass of the forward: writes each logical
+// key tile of 64 keys transposed, as 128 channel rows of 64 keys, the keys of
+// every 16-key chunk in the A.V product's reduction order; keys past a tile's
+// valid count are zero.
+constexpr int kVtileElems = kHeadDim * kFwdBN;  // FP16 values per V^T tile
+struct VtileArgs {
   View<const uint16_t> v;  // BF16 [B,S,H,128] (B of this launch)
-  uint16_t* out;           // FP16 dense [B,H,S,128]
-  int S, H, T_txt;
+  uint16_t* out;           // FP16 [B][H][nt_max][128][64]
+  int H, T_txt, T_img, nt_max;
   int txt_len[kMaxBatchPerLaunch];
 };
-__global__ void v_f16_kernel(VcastArgs a);
+__global__ void v_tiles_kernel(VtileArgs a);
 __global__ void attn_bwd_dq_kernel(BwdArgs a);
 __global__ void attn_bwd_dk_kernel(BwdArgs a);
 __global__ void attn_bwd_dv_kernel(BwdArgs a);

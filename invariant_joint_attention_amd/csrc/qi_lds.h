@@ -141,6 +141,46 @@ __device__ __forceinline__ bf16x8 tr_frag(uint32_t tb) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// V^T tiles of the forward: 128 channel rows x 64 keys in FP16, one 128-byte
+// line per channel, the keys of each 16-key chunk already in the A.V
+// reduction order (written so by the conversion pass).  Logical 16-byte chunk
+// j of row d (keys 8j .. 8j+7 of that order) lives at chunk j ^ ((d >> 1) & 7):
+// a 16-lane group of fragment reads covers 16 consecutive rows at one logical
+// chunk, i.e. 8 distinct chunks in each of two 128-byte row parities, which
+// are the 64 banks once.
+constexpr int kVtRowB = 128;
+
+// Fragment of channel rows 32*db .. 32*db+31 and 16-key chunk c2: lane l
+// reads row 32*db + l%32, logical chunk 2*c2 + l/32.  With s = ((l%32) >> 1) & 7
+// the physical chunk is 2*(c2 ^ s/2) + ((l/32) ^ s)%2, so the address is
+// vt_base ^ (c2 << 5) plus the immediate 32*db rows.
+__device__ __forceinline__ uint32_t vt_base(uint32_t tile, int lane) {
+  const int lr = lane & 31, hh = lane >> 5;
+  const int s = (lr >> 1) & 7;
+  return tile + lr * kVtRowB + 32 * (s >> 1) + 16 * ((hh ^ s) & 1);
+}
+
+// Tile fill from a contiguous 16 KiB source tile [128][64]: wave `sub` (0..3)
+// fills channel rows 32*sub .. 32*sub+31, 8 rows (1 KiB) per instruction;
+// lane l writes LDS slot l of the block, i.e. physical chunk l%8 of row
+// 8i + l/8, and fetches the logical chunk the swizzle maps there, which
+// depends on the lane and on i%2 only.
+struct VtOff {
+  uint32_t o[2];
+};
+__device__ __forceinline__ VtOff vt_offsets(int lane) {
+  VtOff r;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) r.o[p] = (uint32_t)((lane >> 3) * kVtRowB + 16 * ((lane & 7) ^ (4 * p + (lane >> 4))));
+  return r;
+}
+__device__ __forceinline__ void load_vt(const uint16_t* src_tile, const VtOff& vo, char* dst, int sub) {
+  const char* base = (const char*)src_tile + sub * 32 * kVtRowB;
+  const uint32_t la = addr_of(dst + sub * 32 * kVtRowB);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(base + i * 8 * kVtRowB, vo.o[i & 1], la + i * 8 * kVtRowB);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads: callers wait
 // for exactly the memory operations the next phase depends on.
 __device__ __forceinline__ void bar() {

@@ -118,8 +118,9 @@ def test_forward_workspace_validation():
     g = geom()
     L = qi.lib()
     ws = L.qi_joint_attn_fwd_workspace(g.ptr())
-    # B*H*S*128 FP16 values, rounded up to 256 bytes
-    assert ws == -(-(g.B * g.H * g.S * 128 * 2) // 256) * 256
+    # B*H*nt FP16 tiles of 64 keys x 128 channels, nt = ceil(T_txt/64) + ceil(h*w/64), rounded up to 256 bytes
+    nt = -(-g.T_txt // 64) + -(-(g.grid_h * g.grid_w) // 64)
+    assert ws == -(-(g.B * g.H * nt * 64 * 128 * 2) // 256) * 256
     assert fwd_call(g, ws=0) == code("QI_E_WORKSPACE")
     assert fwd_call(g, ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
     assert fwd_call(g, ws=region(5) + 16) == code("QI_E_ALIGN")
