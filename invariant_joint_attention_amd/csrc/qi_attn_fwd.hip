@@ -43,27 +43,25 @@
 //
 // Schedule (free; does not change any bit):
 //  * Workgroup = 8 waves x 32 query rows of one (b, h).  Waves w and w+4 run
-//    on the same SIMD.  Group 0 (waves 0-3) and group 1 (waves 4-7) alternate
-//    between a matrix phase (P*V of tile t plus the scores of tile t+1, 32
-//    MFMAs) and a softmax phase (VALU only), one workgroup barrier per phase,
-//    so each SIMD has one wave issuing MFMAs while its partner runs the
-//    softmax.  Group 1 starts one barrier later; both run 2*nt + 1 barriers.
-//  * LDS: K tiles in kbuf[j % 3], V^T tiles in vbuf[j % 3], 96 KiB.  K rows
-//    are unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key
+//    on the same SIMD.  A wave alternates a softmax block (VALU only) and a
+//    matrix block (P*V of tile t plus the scores of tile t+1, 32 MFMAs); group
+//    0 (waves 0-3) and group 1 (waves 4-7) are half a tile apart, with one
+//    workgroup barrier per tile, so each SIMD has one wave issuing MFMAs
+//    while its partner runs the softmax; the switch in mid-tile is
+//    self-timed (details at the schedule section below).
+//  * LDS: K tiles and V^T tiles in rings of four (128 KiB).  K rows are
+//    unpadded 256-byte lines whose 16-byte chunks are XOR-swizzled by key
 //    (swizzle bits 2-3 from key bits 0-1, bits 0-1 from key bits 2-3); V^T
 //    tiles are 128 channel lines of 128 bytes swizzled by channel/2.  The K
 //    and V^T fragment reads (one ds_read_b128 each, 16 rows per 16-lane
 //    group) and the contiguous direct-load writes meet no LDS bank conflict
 //    on the 64 banks.  Tiles are filled by direct global->LDS loads
-//    (global_load_lds_dwordx4) issued in the softmax phase of tile t: group
-//    0 loads V_{t+1}, group 1 loads K_{t+2}; each waits for its loads
-//    (vmcnt) at the end of its next matrix phase, a barrier before the tile
-//    is read.  Three buffers are needed because group 0's softmax phase runs
-//    while group 1 still reads the tiles of tile t-1.
-//  * The softmax phase ends with P rounded to FP16, so one FP32 score buffer
-//    suffices: the matrix phase accumulates the next tile's scores into it.
-//  * The matrix phase issues its LDS reads as inline asm two steps ahead of
-//    use and waits for each step's reads with an exact lgkmcnt; the direct
+//    (global_load_lds_dwordx4), group 0 the K tiles and group 1 the V^T
+//    tiles, at the start of a softmax block, three tiles ahead.
+//  * The softmax block ends with P rounded to FP16, so one FP32 score buffer
+//    suffices: the matrix block accumulates the next tile's scores into it.
+//  * The matrix block issues its LDS reads as inline asm three steps ahead of
+//    use and waits for each step's read with an exact lgkmcnt; the direct
 //    loads are inline asm too, so the compiler neither inserts waits for
 //    them before unrelated LDS reads nor keeps 64-bit addresses for them.
 #include "qi_common.h"
@@ -109,71 +107,129 @@ __device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, i
   }
 }
 
-// Per-lane LDS addresses of the matrix phase, relative to K buffer 0 and V
-// buffer 0: eight K row-fragment bases (one per 16-channel chunk kk) and
-// four V^T fragment bases (one per 16-key chunk c2).  The 32-key block and
-// the 32-channel block go into the reads' immediate offsets and each matrix
-// phase adds its buffers' offsets; the XOR patterns touch address bits 5-7
-// only, below the 1 KiB-aligned buffer starts, so base ^ pattern + offset is
-// exact.
+// ---------------------------------------------------------------- schedule
+// Workgroup = 8 waves x 32 query rows of one (b, h); waves w and w+4 share a
+// SIMD and belong to group 0 (waves 0-3) and group 1 (waves 4-7).  A wave's
+// work per tile alternates a matrix block MM(t) = P*V of tile t and the
+// scores of tile t+1 (32 MFMAs) with a softmax block SM(t+1) (VALU only:
+// mask, row max, lazy reference-max move and rescale, p = exp2, row sum,
+// FP16 packing of P).  One workgroup barrier B_t per tile; between B_t and
+// B_{t+1}
+//   group 0 runs MM(t), then SM(t+1);
+//   group 1 runs SM(t),  then MM(t);
+// so on each SIMD one wave issues MFMAs while its partner runs the softmax,
+// and the mid-tile switch is self-timed: a group that finishes its softmax
+// early starts its matrix block beside the partner's, which keeps the MFMA
+// pipe busy until the barrier as long as a softmax block is shorter than a
+// matrix block.
+//
+// LDS: K tiles in a ring of four, V^T tiles in a ring of four (128 KiB).
+// Between B_t and B_{t+1} both groups read V tile t and K tile t+1; tiles
+// are loaded four (K) and three (V) tiles ahead and each wave has its own
+// loads of the tile before landed by the next barrier, so every tile is
+// visible one tile before it is read: a matrix block's first fragments are
+// read at the end of the softmax block before it, across the barrier for
+// group 0.
+struct St {
+  f32x16 acc[4];  // O^T [32-channel block], FP32 (V scaled by 2^-8)
+  f32x16 s[2];    // scores [32-key block]
+  u32x4 p[4];     // FP16 P [16-key chunk]
+  bf16x8 q[8];    // Q [16-channel chunk]
+  float m_used, l;
+};
+
+// Per-lane LDS fragment addresses relative to K buffer 0 / V buffer 0: eight
+// K row-fragment bases (one per 16-channel chunk kk) and four V^T bases (one
+// per 16-key chunk c2); the 32-key block / 32-channel block go into the
+// reads' immediate offsets and each block adds its buffers' offsets (the XOR
+// patterns touch address bits 4-6 only, below the 1 KiB-aligned buffers).
 struct Addr {
   uint32_t k[8], v[4];
 };
-__device__ __forceinline__ Addr make_addr(uint32_t lds0, int lane) {
+
+constexpr int kKRing = 4, kVRing = 4;  // LDS ring depth (tiles), K and V^T
+constexpr uint32_t kVRingOfs = kKRing * kTileB;
+constexpr int kAhead = 3;  // fragments read ahead of their step (ring of 4)
+
+// this block's addresses: the bases plus its K and V^T buffer offsets
+__device__ __forceinline__ Addr block_addr(const Addr& ad, uint32_t kofs, uint32_t vofs) {
   Addr a;
-  const uint32_t rb = row_base(lds0, lane), tb = vt_base(lds0 + 3 * kTileB, lane);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) a.k[kk] = rb ^ (uint32_t)(kk << 5);
+  for (int i = 0; i < 8; ++i) a.k[i] = ad.k[i] + kofs;
 #pragma unroll
-  for (int c2 = 0; c2 < 4; ++c2) a.v[c2] = tb ^ (uint32_t)(c2 << 5);
-  // opaque: the compiler keeps the twelve addresses instead of
-  // re-deriving them with VALU work inside the loop
-#pragma unroll
-  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a.k[i]));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(a.v[i]));
+  for (int i = 0; i < 4; ++i) a.v[i] = ad.v[i] + vofs;
   return a;
 }
 
-// K fragment of score step k (block kb = k/8, chunk kk = k%8).
-template <int k>
-__device__ __forceinline__ bf16x8 kfrag(const Addr& ad) {
-  constexpr int kk = k & 7, kb = k >> 3;
-  return __builtin_bit_cast(bf16x8, ds_b128<kb * 32 * kRowB>(ad.k[kk]));
-}
-// V^T fragment of P*V step k (16-key chunk c2 = k/4, 32-channel block d = k%4):
-// channel rows 32*d .. 32*d+31, one 16-byte read per lane.
-template <int k>
-__device__ __forceinline__ f16x8 vfrag(const Addr& ad) {
-  constexpr int c2 = k >> 2, d = k & 3;
-  return __builtin_bit_cast(f16x8, ds_b128<d * 32 * kVtRowB>(ad.v[c2]));
-}
-
-struct State {
-  f32x16 acc[4];
-  f32x16 s[2];   // scores of one 64-key tile (two 32-key blocks), FP32
-  u32x4 ph[4];   // FP16 P of the tile's four 16-key chunks
-  bf16x8 q[8];
-  float m_used, l_lane;
+// Matrix block step k.  With P*V (kPV) the block alternates P*V and score
+// products: even k = P*V of chunk k/8, channel block (k/2)%4; odd k (and
+// every k of a scores-only block) = scores of 32-key block kb, chunk kk.
+// Fragment k of the block is the operand read for step k.
+template <bool kPV, int k>
+struct MmStep {
+  static constexpr bool pv = kPV && (k & 1) == 0;
+  static constexpr int c2 = k >> 3, d = (k >> 1) & 3;            // P*V step
+  static constexpr int ks = kPV ? (k >> 1) : k;                  // score step index
+  static constexpr int kb = ks >> 3, kk = ks & 7;                // score step
 };
+template <bool kPV, int k>
+__device__ __forceinline__ u32x4 read_frag(const Addr& ad) {
+  using M = MmStep<kPV, k>;
+  if constexpr (M::pv)
+    return ds_b128<M::d * 32 * kVtRowB>(ad.v[M::c2]);
+  else
+    return ds_b128<M::kb * 32 * kRowB>(ad.k[M::kk]);
+}
 
-// S^T = K Q^T for one 64-key tile (16 MFMAs, no P*V work).
-__device__ __forceinline__ void s_only(State& st, const char* kbuf, int lane) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.s[kb][r] = 0.f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int kk = k >> 1, kb = k & 1;
-    const bf16x8 kv = *(const bf16x8*)(kbuf + off(32 * kb + (lane & 31), 2 * kk + (lane >> 5)));
-    st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
+// Issue the first kAhead reads of a matrix block (ring slots 0..kAhead-1).
+template <bool kPV, int f>
+__device__ __forceinline__ void mm_prefetch(u32x4 (&fr)[4], const Addr& ad) {
+  if constexpr (f < kAhead) {
+    fr[f] = read_frag<kPV, f>(ad);
+    mm_prefetch<kPV, f + 1>(fr, ad);
   }
 }
 
-// Softmax of one tile: mask, row max, lazy reference-max move, p = exp2, row
-// sum; then P rounded to FP16 (RNE) for the P*V products.
-__device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
+// Matrix block: NF steps (32 with P*V and scores, 16 with one of them); the
+// first kAhead fragments were issued before; each step issues the read
+// kAhead ahead and waits for its own with an exact lgkmcnt.
+template <bool kPV, bool kS, int k>
+__device__ __forceinline__ void mm_step(St& st, u32x4 (&fr)[4], const Addr& ad) {
+  constexpr int NF = (kPV ? 16 : 0) + (kS ? 16 : 0);
+  if constexpr (k < NF) {
+    constexpr int fn = k + kAhead;
+    if constexpr (fn < NF) fr[fn & 3] = read_frag<kPV && kS, fn>(ad);
+    constexpr int issued_after = NF - 1 - k;
+    constexpr int later = issued_after < kAhead ? issued_after : kAhead;
+    u32x4& v = fr[k & 3];
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(later));
+    using M = MmStep<kPV && kS, k>;
+    constexpr bool pv = kS ? M::pv : true;  // a P*V-only block: every step is P*V
+    if constexpr (pv) {
+      constexpr int c2 = kS ? M::c2 : (k >> 2), d = kS ? M::d : (k & 3);
+      st.acc[d] = mfma32h(__builtin_bit_cast(f16x8, fr[k & 3]), __builtin_bit_cast(f16x8, st.p[c2]), st.acc[d]);
+    } else {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, fr[k & 3]);
+      if constexpr (M::kk == 0)
+        st.s[M::kb] = mfma32(kf, st.q[M::kk], f32x16{});
+      else
+        st.s[M::kb] = mfma32(kf, st.q[M::kk], st.s[M::kb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mm_step<kPV, kS, k + 1>(st, fr, ad);
+  }
+}
+template <bool kPV, bool kS>
+__device__ __forceinline__ void mm_block(St& st, u32x4 (&fr)[4], const Addr& ad) {
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  mm_step<kPV, kS, 0>(st, fr, ad);
+  __builtin_amdgcn_s_setprio(0);
+}
+// Softmax block of one tile: mask, row max, lazy reference-max move (and
+// rescale of acc, which holds P*V of the tiles before), p = exp2, row sum;
+// then P rounded to FP16 (RNE) for the P*V products.
+__device__ __forceinline__ void sm_block(St& st, int cur_valid, int hh) {
   f32x16 (&sx)[2] = st.s;
   if (cur_valid < kFwdBN) {
     // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
@@ -189,12 +245,16 @@ __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sx[0][r]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[1][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  {
+    const uint32_t u = __float_as_uint(mt);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   const bool move = mt > st.m_used + kTauRaw;
   const float m_new = move ? mt : st.m_used;
   if (__any(move)) {
     const float alpha = (m_new == st.m_used) ? 1.0f : __builtin_amdgcn_exp2f((st.m_used - m_new) * kC);
-    st.l_lane = st.l_lane * alpha;
+    st.l = st.l * alpha;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -210,94 +270,24 @@ __device__ __forceinline__ void softmax_tile(State& st, int cur_valid, int hh) {
       sx[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[kb][r], kC, -mc));
       ts = ts + sx[kb][r];
     }
-  st.l_lane = st.l_lane + ts;
+  st.l = st.l + ts;
 #pragma unroll
   for (int c2 = 0; c2 < 4; ++c2)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int kb = c2 >> 1, r = 8 * (c2 & 1) + 2 * w;
-      st.ph[c2][w] = pack_f16x2(sx[kb][r], sx[kb][r + 1]);
+      st.p[c2][w] = pack_f16x2(sx[kb][r], sx[kb][r + 1]);
     }
-}
-
-// Matrix phase: O^T += V^T P^T per 16-key chunk and, when kS, S^T of the
-// next tile interleaved (16 + 16 MFMAs).  Step k's fragments are read kPre
-// steps ahead; sched barriers pin that order and each step waits only for
-// its own reads.  The first score MFMA of each 32-key block starts from a
-// zero accumulator.
-constexpr int kPre = 2;
-
-template <bool kS, int k>
-__device__ __forceinline__ void mm_issue(f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
-  if constexpr (k < 16) {
-    vr[k % (kPre + 1)] = vfrag<k>(ad);
-    if constexpr (kS) kr[k % (kPre + 1)] = kfrag<k>(ad);
-  }
-}
-
-template <bool kS, int k>
-__device__ __forceinline__ void mm_step(State& st, f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
-  if constexpr (k < 16) {
-    mm_issue<kS, k + kPre>(vr, kr, ad);
-    // reads issued after step k's own: those of steps k+1 .. k+kPre
-    constexpr int per = kS ? 2 : 1;
-    constexpr int ahead = (15 - k) < kPre ? (15 - k) : kPre;
-    constexpr int later = per * ahead;
-    f16x8& vv = vr[k % (kPre + 1)];
-    bf16x8& kv = kr[k % (kPre + 1)];
-    if constexpr (kS)
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vv), "+v"(kv) : "i"(later));
-    else
-      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(vv) : "i"(later));
-    constexpr int c2 = k >> 2, d = k & 3;
-    st.acc[d] = mfma32h(vv, __builtin_bit_cast(f16x8, st.ph[c2]), st.acc[d]);
-    if constexpr (kS) {
-      constexpr int kb = k >> 3, kk = k & 7;
-      if constexpr (kk == 0)
-        st.s[kb] = mfma32(kv, st.q[kk], f32x16{});
-      else
-        st.s[kb] = mfma32(kv, st.q[kk], st.s[kb]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mm_step<kS, k + 1>(st, vr, kr, ad);
-  }
-}
-
-template <bool kS, int k>
-__device__ __forceinline__ void mm_prefetch(f16x8 (&vr)[kPre + 1], bf16x8 (&kr)[kPre + 1], const Addr& ad) {
-  if constexpr (k < kPre) {
-    mm_issue<kS, k>(vr, kr, ad);
-    mm_prefetch<kS, k + 1>(vr, kr, ad);
-  }
-}
-
-// Matrix phase of tile t: V_t in V buffer t % 3, K_{t+1} in K buffer
-// (t + 1) % 3; kofs / vofs are those buffers' byte offsets (wave-uniform).
-template <bool kS>
-__device__ __forceinline__ void mm_tile(State& st, const Addr& ad, uint32_t kofs, uint32_t vofs) {
-  Addr a2;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a2.k[i] = ad.k[i] + kofs;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a2.v[i] = ad.v[i] + vofs;
-  f16x8 vr[kPre + 1];
-  bf16x8 kr[kPre + 1];
-  __builtin_amdgcn_sched_barrier(0);
-  mm_prefetch<kS, 0>(vr, kr, a2);
-  __builtin_amdgcn_sched_barrier(0);
-  mm_step<kS, 0>(st, vr, kr, a2);
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[6 * kTileB];
-  char* const kbase = smem;
-  char* const vbase = smem + 3 * kTileB;
+  __shared__ __attribute__((aligned(1024))) char smem[(kKRing + kVRing) * kTileB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
-  const int grp = wave >> 2, sub = wave & 3;
+  const int grp = wave >> 2;
   const int lr = lane & 31, hh = lane >> 5;
 
   int bh, qt;
@@ -314,13 +304,12 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   const int b = bh / a.H, h = bh - b * a.H;
   const int L = a.txt_len[b];
   const int qrow = qt * (kFwdWaves * kFwdRowsPerWave) + wave * kFwdRowsPerWave + lr;
-  const bool qvalid = qrow < a.S;
 
-  State st;
+  St st;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     u32x4 z = {0u, 0u, 0u, 0u};
-    if (qvalid) z = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
+    if (qrow < a.S) z = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
     st.q[kk] = __builtin_bit_cast(bf16x8, z);
   }
 #pragma unroll
@@ -328,75 +317,121 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[d][r] = 0.f;
   st.m_used = -INFINITY;
-  st.l_lane = 0.f;
+  st.l = 0.f;
 
   const int ntxt = (L + kFwdBN - 1) / kFwdBN;
   const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
-  auto kbuf = [&](int j) { return kbase + (j % 3) * kTileB; };
-  auto vbuf = [&](int j) { return vbase + (j % 3) * kTileB; };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  auto kbuf = [&](int j) { return smem + (j % kKRing) * kTileB; };
+  auto vbuf = [&](int j) { return smem + kVRingOfs + (j % kVRing) * kTileB; };
+  auto kofs = [&](int j) { return (uint32_t)((j % kKRing) * kTileB); };
+  auto vofs = [&](int j) { return (uint32_t)((j % kVRing) * kTileB); };
   auto valid_of = [&](int j) {
     int k0, nv;
     tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
     return nv;
   };
+  // Group 0 loads whole K tiles, group 1 whole V^T tiles: wave `sub` of a
+  // group fills 16 K rows (four loads of 4 rows) or 32 V^T channel rows
+  // (four loads of 8 rows).  K rows past the tile's valid count repeat its
+  // last valid row (their scores are masked), so every load is issued.
+  const int sub = wave & 3;
   const RowOff ko = row_offsets(a.k.ss, lane);
-  const VtOff vo = vt_offsets(lane);
-  const uint16_t* const vt_bh = a.vt + ((int64_t)b * a.H + h) * a.nt_max * kVtileElems;
   auto load_k = [&](int j) {
     int k0, nv;
     tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
-    load_rows(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
+    const int r0 = 16 * sub;
+    const uint32_t la = addr_of(kbuf(j) + r0 * kRowB);
+    if (nv >= r0 + 16) {
+      const char* base = (const char*)(a.k.p + (int64_t)b * a.k.sb + (int64_t)h * a.k.sh + (int64_t)(k0 + r0) * a.k.ss);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(base, ko.o[i], la + 4 * i * kRowB);
+    } else {
+      const int rbase = r0 < nv ? r0 : nv - 1;  // a valid source row
+      const char* base =
+          (const char*)(a.k.p + (int64_t)b * a.k.sb + (int64_t)h * a.k.sh + (int64_t)(k0 + rbase) * a.k.ss);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kl = 4 * i + (lane >> 4);            // LDS row within the wave's 16
+        const int src = min(r0 + kl, nv - 1) - rbase;  // source row relative to the base, >= 0
+        const int chunk = (lane & 15) ^ swz(kl);
+        dma16(base, (uint32_t)(src * (uint32_t)a.k.ss + 8 * chunk) * 2u, la + 4 * i * kRowB);
+      }
+    }
   };
+  const VtOff vo = vt_offsets(lane);
+  const uint16_t* const vt_bh = a.vt + ((int64_t)b * a.H + h) * a.nt_max * kVtileElems;
   auto load_v = [&](int j) { load_vt(vt_bh + (int64_t)j * kVtileElems, vo, vbuf(j), sub); };
 
-  // prologue: K_0, V_0 (group 0) and K_1 (group 1)
-  if (grp == 0) {
-    load_k(0);
-    load_v(0);
-  } else if (nt > 1) {
-    load_k(1);
+  Addr ad;
+  {
+    const uint32_t rbase = row_base(lds0, lane), vbase = vt_base(lds0 + kVRingOfs, lane);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) ad.k[kk] = rbase ^ (uint32_t)(kk << 5);
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) ad.v[c2] = vbase ^ (uint32_t)(c2 << 5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(ad.k[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(ad.v[i]));
+  }
+
+  // Tiles 0..2 of K and V up front.  Then K tile j is loaded by group 0
+  // between B_{j-4} and B_{j-3} (at the start of its softmax block SM(j-3),
+  // beside group 1's matrix block) and V tile j by group 1 between B_{j-3}
+  // and B_{j-2} (at the start of its SM(j-3), beside group 0's matrix
+  // block).  At every barrier a wave has its loads issued before the
+  // barrier before landed, so a tile is visible to every wave one barrier
+  // interval before it is read, and a buffer is refilled only after the
+  // interval that last read it.
+  for (int j = 0; j < 3 && j < nt; ++j) {
+    if (grp == 0) load_k(j);
+    else load_v(j);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   bar();
 
-  const Addr ad = make_addr((uint32_t)(uintptr_t)(lds_char*)smem, lane);
-  // one tile with a successor: group 0 loads V_{t+1}, group 1 K_{t+2};
-  // softmax; matrix phase; each group waits for its own loads
-  auto tile = [&](int t) {
-    if (grp == 1) {
-      if (t + 2 < nt) load_k(t + 2);
-    } else {
-      load_v(t + 1);
-    }
-    softmax_tile(st, valid_of(t), hh);
-    bar();
-    __builtin_amdgcn_s_setprio(1);
-    mm_tile<true>(st, ad, ((t + 1) % 3) * kTileB, (t % 3) * kTileB);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
+  u32x4 fr[4];
+  // scores of tile 0, both groups
+  {
+    const Addr a0 = block_addr(ad, kofs(0), 0);
+    mm_prefetch<false, 0>(fr, a0);
+    mm_block<false, true>(st, fr, a0);
+  }
+  // B_t: this wave's loads issued before B_{t-1} have landed (the four
+  // issued since may still be in flight), then the barrier.
+  auto barrier_at = [&](int t, bool issued_since) {
+    if (issued_since)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     bar();
   };
-
-  // Both groups run the same sequence; group 1 starts one barrier later, so
-  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
-  if (grp == 1) bar();
-  __builtin_amdgcn_s_setprio(1);
-  s_only(st, kbuf(0), lane);
-  __builtin_amdgcn_s_setprio(0);
-  bar();
-  for (int t = 0; t + 1 < nt; ++t) tile(t);
-  softmax_tile(st, valid_of(nt - 1), hh);
-  bar();
-  __builtin_amdgcn_s_setprio(1);
-  mm_tile<false>(st, ad, 0, ((nt - 1) % 3) * kTileB);
-  __builtin_amdgcn_s_setprio(0);
-  if (grp == 0) bar();
+  // Each wave runs SM(t), MM(t) for t = 0 .. nt-1; group 1 passes B_t
+  // before SM(t), group 0 between SM(t) and MM(t).
+  for (int t = 0; t < nt; ++t) {
+    if (grp == 1) {
+      barrier_at(t, t > 0 && t + 2 < nt);  // V tile t+2 was issued after B_{t-1}
+      if (t + 3 < nt) load_v(t + 3);
+    } else {
+      if (t + 3 < nt) load_k(t + 3);
+    }
+    sm_block(st, valid_of(t), hh);
+    // MM(t) reads V tile t and K tile t+1 (for t = nt-1 a stale K buffer:
+    // those scores are never used); its first fragments now
+    const Addr am = block_addr(ad, kofs(t + 1), vofs(t));
+    mm_prefetch<true, 0>(fr, am);
+    if (grp == 0) barrier_at(t, t + 3 < nt);  // K tile t+3, issued just now
+    mm_block<true, true>(st, fr, am);
+  }
 
   // ---- epilogue: O = acc / l, one RNE cast; LSE in natural log
-  const float l_tot = st.l_lane + __shfl_xor(st.l_lane, 32);
+  const uint32_t lu = __float_as_uint(st.l);
+  const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   // acc holds sum_j p_j v_j 2^-8: divide by l * 2^-8 (exact scaling)
   const float l_div = l_tot * kVScale;
-  if (qvalid) {
+  if (qrow < a.S) {
     uint16_t* orow = a.o.row(b, qrow, h);
     float* frow = a.of ? a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim : nullptr;
 #pragma unroll

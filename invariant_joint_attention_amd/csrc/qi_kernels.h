@@ -39,7 +39,7 @@ struct DgainFoldArgs {
 
 // Forward attention.  One launch covers up to kMaxBatchPerLaunch rows.
 constexpr int kFwdBN = 64;        // key tile width (frozen: part of the arithmetic contract)
-constexpr int kFwdWaves = 8;      // waves per workgroup: two groups of 4 that alternate phases
+constexpr int kFwdWaves = 8;      // waves per workgroup, two per SIMD
 constexpr int kFwdRowsPerWave = 32;
 // Largest K/V sequence stride (elements) the forward's 32-bit row offsets cover.
 constexpr int64_t kFwdMaxRowStride = int64_t(1) << 26;
