@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="1024sq")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--unfused-steps", type=int, default=10,
+                    help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
     return ap.parse_args()
 
 
@@ -172,11 +174,72 @@ def main():
         out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
                            "algorithmic_flops": bflops}
 
+    if args.unfused_steps > 0:
+        out["unfused_fwd"] = bench_unfused(qi, torch, np, wl, geo, qp, kp, g["v"], args.unfused_steps, fwd_ms)
+
     # ---------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, qp, kp, o, lse, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps, fused_ms):
+    """The three unfused operators on the same inputs, each timed with HIP
+    events on the launch stream, against the HBM roofline of the arrays each
+    one reads and writes (scores FP32 and P FP16 over all key slots, the tile
+    factors, V through its FP16 tile pass, O)."""
+    dev = q.device
+    B, H, S = wl.B, wl.H, wl.S
+    Kp = qi.key_slots(geo)
+    nt = Kp // 64
+    s = torch.empty((B, H, S, Kp), dtype=torch.float32, device=dev)
+    p = torch.empty((B, H, S, Kp), dtype=torch.float16, device=dev)
+    alpha = torch.empty((B, H, S, nt), dtype=torch.float32, device=dev)
+    l = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(qi.fwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
+    act = 2 * B * S * H * 128  # one BF16 [B,S,H,128] tensor
+    rows = B * H * S
+    nbytes = {
+        "qk_gemm": 2 * act + 4 * rows * Kp,
+        "softmax": 4 * rows * Kp + 2 * rows * Kp + 4 * rows * nt + 8 * rows,
+        "av_gemm": 2 * rows * Kp + 4 * rows * nt + 4 * rows + act + 2 * 2 * B * H * nt * 64 * 128 + act,
+    }
+    ev = {n: [] for n in nbytes}
+
+    def run(timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if timed:
+            e[0].record()
+        qi.joint_attn_qk_gemm(q, k, geo, scores=s)
+        if timed:
+            e[1].record()
+        qi.joint_attn_softmax(s, geo, p=p, alpha=alpha, l=l, lse=lse)
+        if timed:
+            e[2].record()
+        qi.joint_attn_av_gemm(p, alpha, l, v, geo, out=o, workspace=ws)
+        if timed:
+            e[3].record()
+            for i, n in enumerate(nbytes):
+                ev[n].append((e[i], e[i + 1]))
+
+    run(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        run(True)
+    torch.cuda.synchronize()
+    res = {"steps": steps, "bound": "hbm", "peak_gbps": PEAK_HBM_GBPS}
+    total = 0.0
+    for n, nb in nbytes.items():
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
+        total += ms
+        gbps = nb / (ms * 1e-3) / 1e9
+        res[n] = {"ms": round(ms, 4), "bytes": nb, "gbps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    res["ms"] = round(total, 4)
+    res["vs_fused"] = round(total / fused_ms, 3)
+    return res
 
 
 def cpu_baseline(wl, inp, qp, kp, o, lse, target_s):

@@ -144,6 +144,70 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
                       float* lse, float* o_f32, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * Unfused forward -- the three attention operators of [Kernel list], rows
+ * joint_attn_qk_gemm, joint_attn_softmax and joint_attn_av_gemm, whose
+ * composition qk_gemm -> softmax -> av_gemm gives O, LSE (and O_f32) equal
+ * byte for byte to qi_joint_attn_fwd on the same inputs (row
+ * joint_attention_fused; [Roadmap], "Numerical requirements": fused kernels
+ * reproduce the unfused result byte for byte).  They hold the same per-row
+ * arithmetic as the fused kernel with the intermediates in HBM.
+ *
+ * Intermediates are dense FP32 / FP16 arrays indexed [b][h][i][slot] for
+ * query row i, with Kp = qi_joint_attn_key_slots() slots per row:
+ * Kp = 64 * nt with nt = ceil(T_txt/64) + ceil(grid_h*grid_w/64) logical key
+ * tiles; slot 64*t + j is key j of tile t of row b, where row b's tiles are
+ * ceil(txt_len[b]/64) text tiles (keys 64t ...) followed by the image tiles
+ * (keys T_txt + 64t' ...).  Slots of keys past a tile's valid count, and
+ * every slot of the tiles past row b's own tile count, are masked.
+ */
+/* Key slots per query row, Kp (0 for an invalid geometry). */
+int64_t qi_joint_attn_key_slots(const qi_geom* geom);
+
+/*
+ * qi_joint_attn_qk_gemm -- raw scores s = q_i . k_j, FP32 accumulation of
+ * BF16 products in a fixed order ([Kernel list], row joint_attn_qk_gemm).
+ * The 1/sqrt(128) scale is applied by qi_joint_attn_softmax (inside the
+ * exponent, as c = log2(e)/sqrt(128)), as the fused kernel applies it.
+ *   q, k     BF16 [B,S,H,128].
+ *   scores   FP32 dense [B][H][S][Kp] output; masked slots are -inf.
+ */
+int qi_joint_attn_qk_gemm(const qi_geom* geom, qi_bshd q, qi_bshd k, float* scores,
+                          hipStream_t stream);
+
+/*
+ * qi_joint_attn_softmax -- masked online softmax over the key tiles in
+ * order, fixed tiling of 64 keys ([Kernel list], row joint_attn_softmax).
+ * Per row and tile t: m_t = m_{t-1}, or the tile max when that exceeds
+ * m_{t-1} by more than 8/c; alpha_t = exp2((m_{t-1} - m_t) c) (exactly 1
+ * where m did not move); p = exp2(s c - m_t c); l = alpha_t l + sum p, the
+ * sum formed as two half sums over the keys 8g + 4h' + {0..3} (h' = 0, 1)
+ * in ascending g, added at the end; LSE = (m c + log2 l) ln 2.
+ *   scores   FP32 dense [B][H][S][Kp] from qi_joint_attn_qk_gemm.
+ *   p        FP16 dense [B][H][S][Kp] output: p rounded to nearest even;
+ *            masked slots 0.
+ *   alpha    FP32 dense [B][H][S][Kp/64] output (1 for unused tiles).
+ *   l        FP32 dense [B][H][S] output: the row sum of the FP32 p.
+ *   lse      FP32 dense [B][H][S] output.
+ */
+int qi_joint_attn_softmax(const qi_geom* geom, const float* scores, void* p, float* alpha,
+                          float* l, float* lse, hipStream_t stream);
+
+/*
+ * qi_joint_attn_av_gemm -- O = (sum_t alpha-rescaled P_t V_t) / l
+ * ([Kernel list], row joint_attn_av_gemm): acc = alpha_t acc + P_t V_t tile
+ * by tile, FP16 P times FP16 v * 2^-8 with FP32 accumulation, then
+ * O = acc / (l 2^-8) rounded once to BF16.
+ *   p, alpha, l  outputs of qi_joint_attn_softmax.
+ *   v        BF16 [B,S,H,128].
+ *   o        BF16 [B,S,H,128] output; o_f32 nullable FP32 dense
+ *            [B,S,H,128] output of the pre-cast O.
+ *   workspace  as for qi_joint_attn_fwd (same size; scratch).
+ */
+int qi_joint_attn_av_gemm(const qi_geom* geom, const void* p, const float* alpha,
+                          const float* l, qi_bshd v, qi_bshd o, float* o_f32, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace qi_joint_attn_bwd needs for this geometry. */
 size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
 

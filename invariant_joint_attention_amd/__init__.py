@@ -22,9 +22,9 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
           5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
 
 # every entry point declared in include/qi.h
-SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_bwd_workspace",
-           "qi_joint_attn_bwd",
-           "qi_last_error", "qi_strict_probe", "qi_trace")
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_key_slots",
+           "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
+           "qi_joint_attn_bwd", "qi_last_error", "qi_strict_probe", "qi_trace")
 
 
 class QiError(RuntimeError):
@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd_workspace.argtypes = [G]
         L.qi_joint_attn_fwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
+        L.qi_joint_attn_key_slots.argtypes = [G]
+        L.qi_joint_attn_key_slots.restype = ctypes.c_int64
+        L.qi_joint_attn_qk_gemm.argtypes = [G, QiBshd, QiBshd, P, S]
+        L.qi_joint_attn_softmax.argtypes = [G, P, P, P, P, P, S]
+        L.qi_joint_attn_av_gemm.argtypes = [G, P, P, P, QiBshd, QiBshd, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_bwd_workspace.argtypes = [G]
         L.qi_joint_attn_bwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_bwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, P, QiBshd, P, P,
@@ -67,7 +72,8 @@ def lib() -> ctypes.CDLL:
         L.qi_last_error.restype = ctypes.c_char_p
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
-        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_bwd", "qi_strict_probe"):
+        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
+                     "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_strict_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,6 +154,53 @@ def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None, wo
                                    _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream()))
     return out, lse
+
+
+def key_slots(geom: Geometry) -> int:
+    """Key slots per query row of the unfused intermediates (64 per logical key tile)."""
+    return int(lib().qi_joint_attn_key_slots(geom.ptr()))
+
+
+def joint_attn_qk_gemm(q, k, geom: Geometry, scores=None):
+    """Raw scores q'.k' as FP32 [B, H, S, key_slots] (masked slots -inf)."""
+    if scores is None:
+        scores = _empty((geom.B, geom.H, geom.S, key_slots(geom)), torch.float32, q)
+    _check(lib().qi_joint_attn_qk_gemm(geom.ptr(), _bshd(q), _bshd(k), _ptr(scores), _stream()))
+    return scores
+
+
+def joint_attn_softmax(scores, geom: Geometry, p=None, alpha=None, l=None, lse=None):
+    """Online softmax over the key tiles of FP32 scores [B, H, S, key_slots].
+    Returns (P FP16 [B,H,S,slots], alpha FP32 [B,H,S,slots/64], l FP32
+    [B,H,S], LSE FP32 [B,H,S])."""
+    B, H, S, Kp = geom.B, geom.H, geom.S, key_slots(geom)
+    p = _empty((B, H, S, Kp), torch.float16, scores) if p is None else p
+    alpha = _empty((B, H, S, Kp // 64), torch.float32, scores) if alpha is None else alpha
+    l = _empty((B, H, S), torch.float32, scores) if l is None else l
+    lse = _empty((B, H, S), torch.float32, scores) if lse is None else lse
+    _check(lib().qi_joint_attn_softmax(geom.ptr(), _ptr(scores), _ptr(p), _ptr(alpha), _ptr(l), _ptr(lse), _stream()))
+    return p, alpha, l, lse
+
+
+def joint_attn_av_gemm(p, alpha, l, v, geom: Geometry, out=None, out_f32=None, workspace=None):
+    """O = (alpha-rescaled sum of P V over the key tiles) / l, BF16 [B,S,H,128]."""
+    if out is None:
+        out = _empty(v.shape, torch.bfloat16, v)
+    if workspace is None:
+        workspace = _empty((max(1, fwd_workspace_bytes(geom)),), torch.uint8, v)
+    _check(lib().qi_joint_attn_av_gemm(geom.ptr(), _ptr(p), _ptr(alpha), _ptr(l), _bshd(v), _bshd(out),
+                                       _ptr(out_f32), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def joint_attn_unfused(q, k, v, geom: Geometry, out_f32=None):
+    """The composition qk_gemm -> softmax -> av_gemm; returns (O, LSE, dict of
+    the intermediates).  Equal byte for byte to ``joint_attn_fwd``."""
+    s = joint_attn_qk_gemm(q, k, geom)
+    p, alpha, l, lse = joint_attn_softmax(s, geom)
+    o = joint_attn_av_gemm(p, alpha, l, v, geom, out_f32=out_f32)
+    return o, lse, dict(scores=s, p=p, alpha=alpha, l=l)
 
 
 def bwd_workspace_bytes(geom: Geometry) -> int:

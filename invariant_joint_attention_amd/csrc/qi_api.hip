@@ -233,6 +233,18 @@ size_t fwd_workspace_bytes(const qi_geom* g) {
   return align256((size_t)g->B * g->H * fwd_nt_max(g) * kVtileElems * 2);
 }
 
+// The unfused operators launch a (query-row block, head, batch) grid.
+int check_unfused_grid(const qi_geom* g) {
+  if (g->H > 65535) return fail(QI_E_UNSUPPORTED, "H=%d above the 65535 heads the unfused operators launch", g->H);
+  return QI_OK;
+}
+dim3 unfused_grid(const qi_geom* g, int nb) {
+  return dim3((unsigned)ceil_div(seq_len(g), kUnfRows), (unsigned)g->H, (unsigned)nb);
+}
+void batch_txt_len(const qi_geom* g, int b0, int nb, int* dst) {
+  for (int i = 0; i < kMaxBatchPerLaunch; ++i) dst[i] = i < nb ? g->txt_len[b0 + i] : 0;
+}
+
 BwdLayout bwd_layout(const qi_geom* g) {
   BwdLayout L;
   const int64_t S = seq_len(g);
@@ -399,6 +411,134 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   return QI_OK;
 }
 
+int64_t qi_joint_attn_key_slots(const qi_geom* geom) {
+  if (check_geom(geom)) return 0;
+  return (int64_t)fwd_nt_max(geom) * kFwdBN;
+}
+
+int qi_joint_attn_qk_gemm(const qi_geom* geom, qi_bshd q, qi_bshd k, float* scores, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom), Kp = (int64_t)fwd_nt_max(geom) * kFwdBN;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_dense(scores, (int64_t)geom->B * geom->H * S * Kp * 4, true, "scores", ext))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = check_unfused_grid(geom))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    QkArgs a;
+    a.q = view_of<const uint16_t>(q, b0);
+    a.k = view_of<const uint16_t>(k, b0);
+    a.s = scores + (int64_t)b0 * geom->H * S * Kp;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.nt_max = fwd_nt_max(geom);
+    batch_txt_len(geom, b0, nb, a.txt_len);
+    hipLaunchKernelGGL(attn_qk_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    if ((rc = launched("attn_qk_kernel"))) return rc;
+  }
+  return QI_OK;
+}
+
+int qi_joint_attn_softmax(const qi_geom* geom, const float* scores, void* p, float* alpha, float* l, float* lse,
+                          hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom), nt_max = fwd_nt_max(geom), Kp = nt_max * kFwdBN;
+  const int64_t rows = (int64_t)geom->B * geom->H * S;
+  if ((rc = check_dense(scores, rows * Kp * 4, false, "scores", ext))) return rc;
+  if ((rc = check_dense(p, rows * Kp * 2, true, "p", ext))) return rc;
+  if ((rc = check_dense(alpha, rows * nt_max * 4, true, "alpha", ext))) return rc;
+  if ((rc = check_dense(l, rows * 4, true, "l", ext))) return rc;
+  if ((rc = check_dense(lse, rows * 4, true, "lse", ext))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = check_unfused_grid(geom))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    const int64_t r0 = (int64_t)b0 * geom->H * S;
+    SoftmaxArgs a;
+    a.s = scores + r0 * Kp;
+    a.p = (uint16_t*)p + r0 * Kp;
+    a.alpha = alpha + r0 * nt_max;
+    a.l = l + r0;
+    a.lse = lse + r0;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.nt_max = (int)nt_max;
+    batch_txt_len(geom, b0, nb, a.txt_len);
+    hipLaunchKernelGGL(attn_softmax_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    if ((rc = launched("attn_softmax_kernel"))) return rc;
+  }
+  return QI_OK;
+}
+
+int qi_joint_attn_av_gemm(const qi_geom* geom, const void* p, const float* alpha, const float* l, qi_bshd v,
+                          qi_bshd o, float* o_f32, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom), nt_max = fwd_nt_max(geom), Kp = nt_max * kFwdBN;
+  const int64_t rows = (int64_t)geom->B * geom->H * S;
+  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
+  if ((rc = check_dense(p, rows * Kp * 2, false, "p", ext))) return rc;
+  if ((rc = check_dense(alpha, rows * nt_max * 4, false, "alpha", ext))) return rc;
+  if ((rc = check_dense(l, rows * 4, false, "l", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+  if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  const size_t ws_need = fwd_workspace_bytes(geom);
+  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < ws_need)
+    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
+  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = check_unfused_grid(geom))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  uint16_t* vt = (uint16_t*)workspace;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    const int64_t r0 = (int64_t)b0 * geom->H * S;
+    AvArgs a;
+    a.p = (const uint16_t*)p + r0 * Kp;
+    a.alpha = alpha + r0 * nt_max;
+    a.l = l + r0;
+    a.vt = vt + (int64_t)b0 * geom->H * nt_max * kVtileElems;
+    a.o = view_of<uint16_t>(o, b0);
+    a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.nt_max = (int)nt_max;
+    batch_txt_len(geom, b0, nb, a.txt_len);
+
+    VtileArgs c;
+    c.v = view_of<const uint16_t>(v, b0);
+    c.out = const_cast<uint16_t*>(a.vt);
+    c.H = geom->H;
+    c.T_txt = geom->T_txt;
+    c.T_img = a.T_img;
+    c.nt_max = (int)nt_max;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
+    hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
+                       c);
+    if ((rc = launched("v_tiles_kernel"))) return rc;
+    hipLaunchKernelGGL(attn_av_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    if ((rc = launched("attn_av_kernel"))) return rc;
+  }
+  return QI_OK;
+}
+
 size_t qi_joint_attn_bwd_workspace(const qi_geom* geom) {
   if (check_geom(geom)) return 0;
   return bwd_layout(geom).total;
@@ -497,7 +637,7 @@ const char* qi_trace(void) {
     snprintf(buf, sizeof buf,
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\",\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
              "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","

@@ -66,6 +66,7 @@
 //    them before unrelated LDS reads nor keeps 64-bit addresses for them.
 #include "qi_common.h"
 #include "qi_kernels.h"
+#include "qi_attn_contract.h"
 #include "qi_lds.h"
 
 #include <type_traits>
@@ -75,37 +76,8 @@ namespace qi {
 namespace {
 
 using namespace lds;
+using namespace attn;
 static_assert(kTileRows == kFwdBN, "forward key tile is one LDS tile");
-// log2(e) / sqrt(128), rounded once to FP32
-constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);
-constexpr float kLn2 = 0.69314718055994530942f;
-// V enters P*V as FP16 of v * 2^-8; the epilogue divides by l * 2^-8.
-constexpr float kVScale = 0x1p-8f;
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-// Two FP32 values -> packed FP16 pair (lo = a), round to nearest even.
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const f16x2 v = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-// Threshold on raw scores for moving the reference max: 8 in the exp2 domain.
-constexpr float kTauRaw = (float)(8.0 / (1.4426950408889634074 / 11.313708498984760390));
-
-__device__ __forceinline__ void tile_bounds(int t, int ntxt, int L, int T_txt, int T_img, int& key0,
-                                            int& nvalid) {
-  if (t < ntxt) {
-    key0 = t * kFwdBN;
-    nvalid = min(kFwdBN, L - key0);
-  } else {
-    const int ti = t - ntxt;
-    key0 = T_txt + ti * kFwdBN;
-    nvalid = min(kFwdBN, T_img - ti * kFwdBN);
-  }
-}
 
 // ---------------------------------------------------------------- schedule
 // Workgroup = 8 waves x 32 query rows of one (b, h); waves w and w+4 share a

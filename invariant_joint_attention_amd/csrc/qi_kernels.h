@@ -92,6 +92,42 @@ struct VtileArgs {
   int txt_len[kMaxBatchPerLaunch];
 };
 __global__ void v_tiles_kernel(VtileArgs a);
+
+// Unfused forward: the three operators whose composition the fused kernel
+// reproduces byte for byte.  Intermediates are dense per (b, h) row-major
+// over the query rows, with Kp = 64 * nt_max key slots per row: slot 64*t + j
+// is key j of logical key tile t (slots of keys past a tile's valid count,
+// and of tiles past the row's tile count, hold the masked value).
+constexpr int kUnfRows = 128;  // query rows per workgroup (4 waves x 32)
+struct QkArgs {
+  View<const uint16_t> q, k;
+  float* s;  // FP32 raw scores q'.k' [B][H][S][Kp] (B of this launch); masked = -inf
+  int S, H, T_txt, T_img, nt_max;
+  int txt_len[kMaxBatchPerLaunch];
+};
+struct SoftmaxArgs {
+  const float* s;  // [B][H][S][Kp]
+  uint16_t* p;     // FP16 P [B][H][S][Kp]; masked = 0
+  float* alpha;    // FP32 rescale factor of tile t [B][H][S][nt_max]; unused tiles = 1
+  float* l;        // FP32 row sum [B][H][S]
+  float* lse;      // FP32 [B][H][S]
+  int S, H, T_txt, T_img, nt_max;
+  int txt_len[kMaxBatchPerLaunch];
+};
+struct AvArgs {
+  const uint16_t* p;
+  const float* alpha;
+  const float* l;
+  const uint16_t* vt;  // FP16 V^T key tiles from v_tiles_kernel [B][H][nt_max][128][64]
+  View<uint16_t> o;
+  float* of;  // nullable dense [B,S,H,128]
+  int S, H, T_txt, T_img, nt_max;
+  int txt_len[kMaxBatchPerLaunch];
+};
+__global__ void attn_qk_kernel(QkArgs a);
+__global__ void attn_softmax_kernel(SoftmaxArgs a);
+__global__ void attn_av_kernel(AvArgs a);
+
 __global__ void attn_bwd_dq_kernel(BwdArgs a);
 __global__ void attn_bwd_dk_kernel(BwdArgs a);
 __global__ void attn_bwd_dv_kernel(BwdArgs a);

@@ -309,6 +309,64 @@ void oracle_attn_fwd_bh(int S, int T_txt, int L, const real* q, const real* k,
   }
 }
 
+/* The three attention operators one at a time [Kernel list, rows
+ * joint_attn_qk_gemm, joint_attn_softmax, joint_attn_av_gemm], for checking
+ * each unfused operator on its own.
+ *
+ * Scaled scores of rows [s0, s1) over all S keys, [s1-s0][S]; masked keys 0. */
+void oracle_attn_scores_bh(int S, int T_txt, int L, const real* q, const real* k,
+                           int s0, int s1, real* s) {
+#pragma omp parallel for schedule(static)
+  for (int i = s0; i < s1; ++i)
+    scores_row(S, T_txt, L, q + (int64_t)i * HD, k, s + (int64_t)(i - s0) * S);
+}
+
+/* Softmax over the valid keys of n rows of scaled scores [n][S]: p [n][S]
+ * (masked entries 0), lse [n]. */
+void oracle_attn_softmax_rows(int n, int S, int T_txt, int L, const real* s, real* p,
+                              real* lse) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; ++i)
+    softmax_row(S, T_txt, L, s + (int64_t)i * S, p + (int64_t)i * S, &lse[i]);
+}
+
+/* The A.V step of the online softmax [Kernel list, row joint_attn_av_gemm;
+ * row joint_attn_softmax: the softmax runs over the key sequence in a fixed
+ * tiling].  Keys of a row with text length L are split into logical tiles of
+ * 64: ceil(L/64) tiles of text keys 64t .. (up to L), then the image keys
+ * T_txt + 64u .. (up to S).  With P[i][t][j] the weight of key j of tile t
+ * and alpha[i][t] the factor that rescales what was accumulated before tile
+ * t:
+ *   acc <- alpha_t * acc + sum_j P[t][j] v_key(t,j)   for t = 0, 1, ...
+ *   o = acc / l.
+ * P [n][nt][64] and alpha [n][nt] for nt tile slots (slots past the row's
+ * tiles, and past a tile's keys, are ignored); l [n]; v [S][128]. */
+void oracle_attn_av_rows(int n, int S, int T_txt, int L, int nt, const real* P,
+                         const real* alpha, const real* l, const real* v, real* o) {
+  const int T_img = S - T_txt;
+  const int ntxt = (L + 63) / 64, nimg = (T_img + 63) / 64;
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; ++i) {
+    real acc[HD];
+    for (int c = 0; c < HD; ++c) acc[c] = 0;
+    for (int t = 0; t < ntxt + nimg && t < nt; ++t) {
+      const real a = alpha[(int64_t)i * nt + t];
+      for (int c = 0; c < HD; ++c) acc[c] = a * acc[c];
+      const int first = t < ntxt ? 64 * t : T_txt + 64 * (t - ntxt);
+      const int end = t < ntxt ? L : S;
+      for (int j = 0; j < 64 && first + j < end; ++j) {
+        const real pj = P[((int64_t)i * nt + t) * 64 + j];
+        const real* vj = v + (int64_t)(first + j) * HD;
+        for (int c = 0; c < HD; ++c) {
+          real pr = pj * vj[c];
+          acc[c] = acc[c] + pr;
+        }
+      }
+    }
+    for (int c = 0; c < HD; ++c) o[(int64_t)i * HD + c] = acc[c] / l[i];
+  }
+}
+
 /* Gradients of the attention slice for upstream dO ([S][128]):
  *   dP = dO V^T ; D_i = sum_c dO_ic O_ic ; dS = P o (dP - D) ;
  *   dq = dS K / sqrt(d) ; dk = dS^T Q / sqrt(d) ; dv = P^T dO.

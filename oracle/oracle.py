@@ -170,6 +170,40 @@ class Oracle:
             lse[b, h] = lb
         return o, lse
 
+    def attn_scores_bh(self, q, k, T_txt, L, s0=0, s1=None):
+        """Scaled scores q_i.k_j / sqrt(128) of one (batch, head) slice, rows
+        [s0, s1) x all S keys; masked keys 0."""
+        q, k = self._r(q), self._r(k)
+        S = q.shape[0]
+        s1 = S if s1 is None else s1
+        s = np.empty((s1 - s0, S), dtype=self.dtype)
+        self.lib.oracle_attn_scores_bh(ctypes.c_int(S), ctypes.c_int(T_txt), ctypes.c_int(L), _ptr(q, self.creal),
+                                       _ptr(k, self.creal), ctypes.c_int(s0), ctypes.c_int(s1), _ptr(s, self.creal))
+        return s
+
+    def attn_softmax_rows(self, s, T_txt, L):
+        """Softmax over the valid keys of score rows s [n, S] (scaled).
+        Returns p [n, S] (masked entries 0) and lse [n]."""
+        s = self._r(s)
+        n, S = s.shape
+        p = np.empty((n, S), dtype=self.dtype)
+        lse = np.empty((n,), dtype=self.dtype)
+        self.lib.oracle_attn_softmax_rows(ctypes.c_int(n), ctypes.c_int(S), ctypes.c_int(T_txt), ctypes.c_int(L),
+                                          _ptr(s, self.creal), _ptr(p, self.creal), _ptr(lse, self.creal))
+        return p, lse
+
+    def attn_av_rows(self, P, alpha, l, v, T_txt, L):
+        """The A.V recurrence over logical 64-key tiles: P [n, nt, 64],
+        alpha [n, nt], l [n], v [S, 128] -> o [n, 128]."""
+        P, alpha, l, v = self._r(P), self._r(alpha), self._r(l), self._r(v)
+        n, nt, _ = P.shape
+        S = v.shape[0]
+        o = np.empty((n, HD), dtype=self.dtype)
+        self.lib.oracle_attn_av_rows(ctypes.c_int(n), ctypes.c_int(S), ctypes.c_int(T_txt), ctypes.c_int(L),
+                                     ctypes.c_int(nt), _ptr(P, self.creal), _ptr(alpha, self.creal),
+                                     _ptr(l, self.creal), _ptr(v, self.creal), _ptr(o, self.creal))
+        return o
+
     def attn_bwd(self, q, k, v, dO, txt_len, T_txt, heads=None):
         """Returns dq', dk', dv [B,S,H,128] (NaN outside ``heads``)."""
         B, S, H, _ = q.shape

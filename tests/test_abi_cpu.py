@@ -210,3 +210,41 @@ def test_row_strides_beyond_32_bit_lane_offsets_are_refused():
         rc = L.qi_joint_attn_bwd(g.ptr(), *views, region(6), dout, region(8), region(9), *grads,
                                  region(14), region(15), None, None, region(20), ws, None)
         assert rc == code("QI_E_UNSUPPORTED") and "stride" in qi.last_error(), qi.last_error()
+
+
+def test_unfused_operators_validation():
+    """The three unfused operators: key-slot count, argument checks before any
+    launch, and the device gate for valid calls."""
+    g = geom()
+    L = qi.lib()
+    nt = -(-g.T_txt // 64) + -(-(g.grid_h * g.grid_w) // 64)
+    assert L.qi_joint_attn_key_slots(g.ptr()) == 64 * nt
+    assert L.qi_joint_attn_key_slots(geom(D=64).ptr()) == 0
+    q = fake_bshd(region(0), g.B, g.S, g.H)
+    k = fake_bshd(region(1), g.B, g.S, g.H)
+    v = fake_bshd(region(2), g.B, g.S, g.H)
+    o = fake_bshd(region(3), g.B, g.S, g.H)
+    # scores
+    assert L.qi_joint_attn_qk_gemm(g.ptr(), q, k, region(4), None) == code("QI_E_UNSUPPORTED")
+    assert L.qi_joint_attn_qk_gemm(g.ptr(), q, k, None, None) == code("QI_E_INVALID")
+    assert L.qi_joint_attn_qk_gemm(g.ptr(), q, k, region(4) + 8, None) == code("QI_E_ALIGN")
+    assert L.qi_joint_attn_qk_gemm(g.ptr(), q, k, region(1), None) == code("QI_E_ALIAS")
+    assert L.qi_joint_attn_qk_gemm(geom(H=70000).ptr(), q, k, region(4), None) == code("QI_E_UNSUPPORTED")
+    # softmax: p, alpha, l, lse are outputs and may overlap nothing
+    sm = lambda s=region(4), p=region(5), a=region(6), l=region(7), e=region(8): \
+        L.qi_joint_attn_softmax(g.ptr(), s, p, a, l, e, None)  # noqa: E731
+    assert sm() == code("QI_E_UNSUPPORTED")
+    assert sm(p=None) == code("QI_E_INVALID")
+    assert sm(a=region(6) + 4) == code("QI_E_ALIGN")
+    assert sm(l=region(8)) == code("QI_E_ALIAS")
+    assert sm(p=region(4)) == code("QI_E_ALIAS")
+    # A.V
+    ws = L.qi_joint_attn_fwd_workspace(g.ptr())
+    av = lambda o=o, ws_ptr=region(9), ws_bytes=ws, of=None: \
+        L.qi_joint_attn_av_gemm(g.ptr(), region(5), region(6), region(7), v, o, of, ws_ptr, ws_bytes, None)  # noqa: E731
+    assert av() == code("QI_E_UNSUPPORTED")
+    assert av(ws_ptr=None) == code("QI_E_WORKSPACE")
+    assert av(ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    assert av(ws_ptr=region(9) + 16) == code("QI_E_ALIGN")
+    assert av(o=fake_bshd(region(5), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    assert av(of=region(7)) == code("QI_E_ALIAS")

@@ -498,3 +498,85 @@ def test_forward_path_composes(o32):
     o, l = o32.attn_fwd(o32.widen(fw["q_bf16"]), o32.widen(fw["k_bf16"]), o32.widen(bv), inp["txt_len"], wl.T_txt)
     assert np.array_equal(o, fw["o"]) and np.array_equal(l, fw["lse"])
     assert fw["o_bf16"].dtype == np.uint16 and fw["o_bf16"].shape == (1, 24, 2, HD)
+
+
+# ------------------------------------------------- attention, one operator at a time
+def _tile_keys(T, L, S):
+    """Keys of each logical 64-key tile of a row with text length L: text
+    tiles from key 0, then image tiles from key T (the key tiling of the
+    online softmax)."""
+    tiles = [list(range(t, min(t + 64, L))) for t in range(0, L, 64)]
+    tiles += [list(range(t, min(t + 64, S))) for t in range(T, S, 64)]
+    return tiles
+
+
+OPERATOR_SHAPES = [  # (T_txt, L, h, w)
+    (8, 5, 4, 4),
+    (70, 67, 9, 9),
+    (0, 0, 13, 11),
+    (130, 130, 3, 2),
+]
+
+
+@pytest.mark.parametrize("shape", OPERATOR_SHAPES)
+def test_operator_scores_and_softmax_match_library(o64, shape):
+    """Scaled scores equal a float64 torch matmul over the valid keys (0 on
+    masked keys); the softmax rows equal scipy's softmax / logsumexp."""
+    T, L, h, w = shape
+    S = T + h * w
+    rng = _rng(11)
+    q, k = rng.standard_normal((S, HD)), rng.standard_normal((S, HD))
+    valid = np.array([j < L or j >= T for j in range(S)])
+    ref = (torch.from_numpy(q) @ torch.from_numpy(k).T).numpy() / math.sqrt(HD)
+    s = o64.attn_scores_bh(q, k, T, L)
+    assert np.abs(s[:, valid] - ref[:, valid]).max() < 1e-12
+    assert (s[:, ~valid] == 0).all()
+    s2 = o64.attn_scores_bh(q, k, T, L, 3, min(S, 9))
+    assert np.array_equal(s2, s[3:min(S, 9)])
+    sm = np.where(valid[None], 5 * s, -np.inf)
+    lse_ref = logsumexp(sm, axis=-1)
+    p, lse = o64.attn_softmax_rows(5 * s, T, L)
+    assert np.abs(p - np.exp(sm - lse_ref[:, None])).max() < 1e-14
+    assert np.abs(lse - lse_ref).max() < 1e-12
+    assert (p[:, ~valid] == 0).all()
+
+
+@pytest.mark.parametrize("shape", OPERATOR_SHAPES)
+def test_operator_av_recurrence(o64, shape):
+    """The A.V recurrence over logical tiles (1) with factors from a running
+    maximum reproduces softmax(s) v from torch SDPA, and (2) for arbitrary
+    P, alpha, l equals the closed form sum_t (prod_{u>t} alpha_u) P_t V_t / l."""
+    T, L, h, w = shape
+    S = T + h * w
+    rng = _rng(12)
+    q, k, v = (rng.standard_normal((S, HD)) for _ in range(3))
+    tiles = _tile_keys(T, L, S)
+    nt = len(tiles) + 1  # one unused slot past the row's tiles
+    s = o64.attn_scores_bh(q, k, T, L)
+    n = S
+    P = np.full((n, nt, 64), np.nan)  # unused slots must be ignored
+    alpha = np.full((n, nt), np.nan)
+    l = np.zeros(n)
+    m = np.full(n, -np.inf)
+    for t, keys in enumerate(tiles):
+        st = s[:, keys]
+        m_new = np.maximum(m, st.max(axis=1))
+        alpha[:, t] = np.exp(m - m_new)
+        P[:, t, :len(keys)] = np.exp(st - m_new[:, None])
+        l = alpha[:, t] * l + P[:, t, :len(keys)].sum(axis=1)
+        m = m_new
+    o = o64.attn_av_rows(P, alpha, l, v, T, L)
+    valid = torch.tensor([j < L or j >= T for j in range(S)])
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                         torch.from_numpy(v)[None], attn_mask=valid[None, None, :].expand(1, S, S))
+    assert np.abs(o - ref[0].numpy()).max() < 1e-12
+
+    Pr = rng.uniform(0, 2, (n, nt, 64))
+    ar = rng.uniform(0.25, 1, (n, nt))
+    lr = rng.uniform(1, 64, n)
+    o = o64.attn_av_rows(Pr, ar, lr, v, T, L)
+    closed = np.zeros((n, HD))
+    for t, keys in enumerate(tiles):
+        w_t = np.prod(ar[:, t + 1:len(tiles)], axis=1)
+        closed += w_t[:, None] * (Pr[:, t, :len(keys)] @ v[keys])
+    assert np.abs(o - closed / lr[:, None]).max() < 1e-12

@@ -106,3 +106,27 @@ def custom(name: str, B: int, H: int, T_txt: int, txt_len, h: int, w: int, seed:
 def bits(t: torch.Tensor):
     """BF16 tensor -> numpy uint16 bit patterns (a view, no arithmetic)."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def score_operands(B: int, H: int, S: int, key_slots: int, seed: int) -> torch.Tensor:
+    """Raw FP32 scores [B, H, S, key_slots] for exercising the softmax operator
+    on its own: row i of tile t is sigma_i * N(0,1) + drift_i * t, with
+    sigma_i uniform in [4, 40) and drift_i uniform in [-80, 80) (raw units,
+    before the 1/sqrt(128) scale), so rows both keep and move their running
+    maximum from tile to tile."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    sig = 4 + 36 * torch.rand(B, H, S, 1, generator=g)
+    drift = -80 + 160 * torch.rand(B, H, S, 1, generator=g)
+    tile = (torch.arange(key_slots) // 64).to(torch.float32)
+    return sig * torch.randn(B, H, S, key_slots, generator=g) + drift * tile
+
+
+def av_operands(B: int, H: int, S: int, key_slots: int, seed: int) -> dict:
+    """Operands of the A.V operator on its own: P FP16 uniform in [0, 2)
+    [B, H, S, key_slots], alpha FP32 uniform in [1/4, 1] [B, H, S, key_slots/64],
+    l FP32 uniform in [1, 64) [B, H, S]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    p = (2 * torch.rand(B, H, S, key_slots, generator=g)).to(torch.float16)
+    alpha = 0.25 + 0.75 * torch.rand(B, H, S, key_slots // 64, generator=g)
+    l = 1 + 63 * torch.rand(B, H, S, generator=g)
+    return dict(p=p, alpha=alpha, l=l)
