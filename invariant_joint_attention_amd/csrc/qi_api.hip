@@ -238,8 +238,8 @@ int check_unfused_grid(const qi_geom* g) {
   if (g->H > 65535) return fail(QI_E_UNSUPPORTED, "H=%d above the 65535 heads the unfused operators launch", g->H);
   return QI_OK;
 }
-dim3 unfused_grid(const qi_geom* g, int nb) {
-  return dim3((unsigned)ceil_div(seq_len(g), kUnfRows), (unsigned)g->H, (unsigned)nb);
+dim3 unfused_grid(const qi_geom* g, int nb, int waves) {
+  return dim3((unsigned)ceil_div(seq_len(g), 32 * waves), (unsigned)g->H, (unsigned)nb);
 }
 void batch_txt_len(const qi_geom* g, int b0, int nb, int* dst) {
   for (int i = 0; i < kMaxBatchPerLaunch; ++i) dst[i] = i < nb ? g->txt_len[b0 + i] : 0;
@@ -426,6 +426,8 @@ int qi_joint_attn_qk_gemm(const qi_geom* geom, qi_bshd q, qi_bshd k, float* scor
   if ((rc = check_dense(scores, (int64_t)geom->B * geom->H * S * Kp * 4, true, "scores", ext))) return rc;
   if ((rc = check_alias(ext))) return rc;
   if ((rc = check_unfused_grid(geom))) return rc;
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
@@ -439,7 +441,7 @@ int qi_joint_attn_qk_gemm(const qi_geom* geom, qi_bshd q, qi_bshd k, float* scor
     a.T_img = geom->grid_h * geom->grid_w;
     a.nt_max = fwd_nt_max(geom);
     batch_txt_len(geom, b0, nb, a.txt_len);
-    hipLaunchKernelGGL(attn_qk_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_qk_kernel, unfused_grid(geom, nb, kQkWaves), dim3(64 * kQkWaves), 0, stream, a);
     if ((rc = launched("attn_qk_kernel"))) return rc;
   }
   return QI_OK;
@@ -475,7 +477,8 @@ int qi_joint_attn_softmax(const qi_geom* geom, const float* scores, void* p, flo
     a.T_img = geom->grid_h * geom->grid_w;
     a.nt_max = (int)nt_max;
     batch_txt_len(geom, b0, nb, a.txt_len);
-    hipLaunchKernelGGL(attn_softmax_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_softmax_kernel, unfused_grid(geom, nb, kSoftmaxWaves), dim3(64 * kSoftmaxWaves), 0, stream,
+                       a);
     if ((rc = launched("attn_softmax_kernel"))) return rc;
   }
   return QI_OK;
@@ -533,7 +536,7 @@ int qi_joint_attn_av_gemm(const qi_geom* geom, const void* p, const float* alpha
     hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
                        c);
     if ((rc = launched("v_tiles_kernel"))) return rc;
-    hipLaunchKernelGGL(attn_av_kernel, unfused_grid(geom, nb), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_av_kernel, unfused_grid(geom, nb, kAvWaves), dim3(64 * kAvWaves), 0, stream, a);
     if ((rc = launched("attn_av_kernel"))) return rc;
   }
   return QI_OK;

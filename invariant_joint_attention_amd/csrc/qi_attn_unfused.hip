@@ -35,15 +35,25 @@
 // by alpha gives the bits of the fused kernel, which skips the rescale
 // where no row of a wave moved its reference max.
 //
-// Launch shape (free): 4 waves x 32 query rows per workgroup, one (b, h)
-// per grid row; operands are read straight from global memory (L2).
+// Launch shapes (free; no bit depends on them):
+//  * scores: 8 waves x 32 query rows; K tiles are staged in LDS (direct
+//    global->LDS loads, double buffered, the fused kernel's swizzled rows) and
+//    shared by the workgroup; a wave's scores go to HBM as 16-byte stores.
+//  * softmax: 4 waves x 32 rows; each wave stages its rows' score tile in LDS
+//    (direct loads of whole 256-byte row pieces, double buffered), reads its
+//    lanes' values back in the register order of the fused kernel, and writes
+//    P through LDS as whole 128-byte row pieces.
+//  * A.V: 8 waves x 32 rows; V^T tiles staged in LDS and shared (double
+//    buffered); each wave stages its rows' P tile in LDS the same way.
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_attn_contract.h"
+#include "qi_lds.h"
 
 namespace qi {
 
 using namespace attn;
+using namespace lds;
 
 namespace {
 
@@ -58,13 +68,36 @@ __device__ __forceinline__ RowTiles row_tiles(const int* txt_len, int b, int T_i
   return r;
 }
 
+// Wait for this wave's LDS reads issued as inline asm, then pin the values
+// behind the wait so that no use is scheduled above it.
+template <int N>
+__device__ __forceinline__ void lds_wait_pin(u32x4 (&f)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
+// One direct global -> LDS load of 4 bytes per lane (lane l's bytes land at
+// LDS byte lds + 4*l), with the conventions of dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const char* base, uint32_t off32, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(off32), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace
 
-__global__ __launch_bounds__(256) void attn_qk_kernel(QkArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kQkWaves * 64) void attn_qk_kernel(QkArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int qrow = blockIdx.x * kUnfRows + wave * 32 + lr;
+  const int qrow = blockIdx.x * (kQkWaves * 32) + wave * 32 + lr;
   const RowTiles rt = row_tiles(a.txt_len, b, a.T_img);
   const int64_t Kp = (int64_t)a.nt_max * kFwdBN;
 
@@ -77,24 +110,50 @@ __global__ __launch_bounds__(256) void attn_qk_kernel(QkArgs a) {
   }
   float* const srow = a.s + (((int64_t)b * a.H + h) * a.S + qrow) * Kp;
 
+  // Waves 0-3 fill the K tiles, 16 rows each; rows past a tile's valid count
+  // are zero in LDS (their scores are masked).
+  const RowOff ro = row_offsets(a.k.ss, lane);
+  auto load = [&](int t) {
+    int k0, nv;
+    tile_bounds(t, rt.ntxt, rt.L, a.T_txt, a.T_img, k0, nv);
+    load_rows(a.k, ro, smem + (t & 1) * kTileB, b, h, k0, nv, wave, lane);
+  };
+  const uint32_t rb0 = row_base(addr_of(smem), lane);
+  if (wave < 4) load(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  bar();
+  if (wave < 4 && rt.nt > 1) load(1);
+
   for (int t = 0; t < a.nt_max; ++t) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
     int nv = 0;
     if (t < rt.nt) {  // uniform over the workgroup
       int key0;
       tile_bounds(t, rt.ntxt, rt.L, a.T_txt, a.T_img, key0, nv);
+      const uint32_t rb = rb0 + (uint32_t)((t & 1) * kTileB);
+      u32x4 f[16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // rows past the valid count repeat the last valid row; their scores are masked
-        const uint16_t* krow = a.k.row(b, key0 + min(32 * kb + lr, nv - 1), h);
+      for (int kk = 0; kk < 8; ++kk) {
+        f[kk] = ds_b128<0>(rb ^ (uint32_t)(kk << 5));
+        f[8 + kk] = ds_b128<32 * kRowB>(rb ^ (uint32_t)(kk << 5));
+      }
+      lds_wait_pin(f);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(krow + 16 * kk + 8 * hh));
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, f[8 * kb + kk]);
           if (kk == 0)
             s[kb] = mfma32(kf, q[0], f32x16{});
           else
             s[kb] = mfma32(kf, q[kk], s[kb]);
         }
+      if (t + 1 < rt.nt) {
+        // tile t+1 landed (loads and zero fills of waves 0-3); every wave is
+        // done with buffer t&1, which then takes tile t+2
+        if (wave < 4) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        bar();
+        if (wave < 4 && t + 2 < rt.nt) load(t + 2);
       }
     }
     if (qrow < a.S) {
@@ -111,31 +170,63 @@ __global__ __launch_bounds__(256) void attn_qk_kernel(QkArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void attn_softmax_kernel(SoftmaxArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hh = lane >> 5;
+// Softmax LDS per wave: two score tiles of 32 rows x 256 bytes (chunk c of
+// row r at chunk c ^ swz(r)) and one P tile of 32 rows x 128 bytes (chunk c
+// of row r at chunk c ^ (r & 7)).
+constexpr int kSmScoreB = 32 * 256, kSmPB = 32 * 128;
+constexpr int kSmWaveB = 2 * kSmScoreB + kSmPB;
+
+__global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(SoftmaxArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSoftmaxWaves * kSmWaveB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int qrow = blockIdx.x * kUnfRows + wave * 32 + (lane & 31);
-  const int qr = min(qrow, a.S - 1);  // rows past S compute on a valid row and store nothing
+  const int row0 = blockIdx.x * (kSoftmaxWaves * 32) + wave * 32;  // the wave's first row
+  const int qrow = row0 + lr;
   const RowTiles rt = row_tiles(a.txt_len, b, a.T_img);
   const int64_t Kp = (int64_t)a.nt_max * kFwdBN;
-  const int64_t row = ((int64_t)b * a.H + h) * a.S + qr;
-  const float* const srow = a.s + row * Kp;
-  uint16_t* const prow = a.p + row * Kp;
-  float* const arow = a.alpha + row * a.nt_max;
+  const int64_t bh = (int64_t)b * a.H + h;
   const bool store = qrow < a.S;
+  char* const wbuf = smem + wave * kSmWaveB;
+  char* const pbuf = wbuf + 2 * kSmScoreB;
+
+  // Rows past S read the last row (their results are not stored).
+  const int base_row = min(row0, a.S - 1);
+  const char* const sbase = (const char*)(a.s + (bh * a.S + base_row) * Kp);
+  uint32_t soff[8];  // load i, lane l: row 4i + l/16, logical chunk (l%16) ^ swz(row)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int rr = min(row0 + r, a.S - 1) - base_row;
+    soff[i] = (uint32_t)rr * (uint32_t)(Kp * 4) + 16u * (uint32_t)((lane & 15) ^ swz(r));
+  }
+  auto load_scores = [&](int t) {
+    const char* src = sbase + (int64_t)t * kFwdBN * 4;
+    const uint32_t dst = addr_of(wbuf + (t & 1) * kSmScoreB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(src, soff[i], dst + 1024u * i);
+  };
+  // this lane's logical chunk 8kb + 2g + hh of row lr sits at chunk (8kb + 2g) ^ (hh ^ swz(lr))
+  const uint32_t frag0 = addr_of(wbuf) + (uint32_t)(lr * 256 + 16 * (hh ^ swz(lr)));
+  uint16_t* const prow0 = a.p + (bh * a.S + row0) * Kp;
+  float* const arow = a.alpha + (bh * a.S + min(qrow, a.S - 1)) * a.nt_max;
 
   float m_used = -INFINITY, l = 0.f;
+  load_scores(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   for (int t = 0; t < rt.nt; ++t) {
+    if (t + 1 < rt.nt) load_scores(t + 1);
+    u32x4 f[8];
+    const uint32_t fb = frag0 + (uint32_t)((t & 1) * kSmScoreB);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = ds_b128<0>(fb ^ (uint32_t)(16 * (8 * (j >> 2) + 2 * (j & 3))));
+    lds_wait_pin(f);
     f32x16 sx[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *(const f32x4*)(srow + kFwdBN * t + 32 * kb + 8 * g + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sx[kb][4 * g + e] = v[e];
-      }
+      for (int e = 0; e < 4; ++e) sx[j >> 2][4 * (j & 3) + e] = __uint_as_float(f[j][e]);
     // exact tile max over the row's 64 slots: this half-row, then the other
     float mt = sx[0][0];
 #pragma unroll
@@ -162,78 +253,152 @@ __global__ __launch_bounds__(256) void attn_softmax_kernel(SoftmaxArgs a) {
         ts = ts + sx[kb][r];
       }
     l = l + ts;
-    if (store) {
+    // P (FP16) through LDS: keys 32kb + 8g + 4hh .. +3 are the 8-byte half hh
+    // of chunk 4kb + g of the 128-byte row piece
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 pv = {pack_f16x2(sx[kb][4 * g], sx[kb][4 * g + 1]),
-                            pack_f16x2(sx[kb][4 * g + 2], sx[kb][4 * g + 3])};
-          *(u32x2*)(prow + kFwdBN * t + 32 * kb + 8 * g + 4 * hh) = pv;
-        }
-      if (hh == 0) arow[t] = alpha;
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 pv = {pack_f16x2(sx[kb][4 * g], sx[kb][4 * g + 1]),
+                          pack_f16x2(sx[kb][4 * g + 2], sx[kb][4 * g + 3])};
+        *(u32x2*)(pbuf + lr * 128 + 16 * ((4 * kb + g) ^ (lr & 7)) + 8 * hh) = pv;
+      }
+    u32x4 po[4];  // store i, lane l: row 8i + l/8, physical chunk l%8
+#pragma unroll
+    for (int i = 0; i < 4; ++i) po[i] = *(const u32x4*)(pbuf + (8 * i + (lane >> 3)) * 128 + 16 * (lane & 7));
+    // scores of tile t+1 landed; the stores of tile t-1 are done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      if (row0 + r < a.S) {
+        const int c = (lane & 7) ^ (r & 7);
+        *(u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * c) = po[i];
+      }
     }
+    if (store && hh == 0) arow[t] = alpha;
   }
-  if (store) {
-    for (int t = rt.nt; t < a.nt_max; ++t) {
-      const u32x2 z = {0u, 0u};
+  // tiles past this row's count: P = 0, alpha = 1
+  for (int t = rt.nt; t < a.nt_max; ++t) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *(u32x2*)(prow + kFwdBN * t + 8 * j + 4 * hh) = z;
-      if (hh == 0) arow[t] = 1.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      if (row0 + r < a.S) *(u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * (lane & 7)) = z;
     }
+    if (store && hh == 0) arow[t] = 1.0f;
   }
   const uint32_t lu = __float_as_uint(l);
   const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   if (store && hh == 0) {
+    const int64_t row = bh * a.S + qrow;
     a.l[row] = l_tot;
     a.lse[row] = (m_used * kC + log2f(l_tot)) * kLn2;
   }
 }
 
-__global__ __launch_bounds__(256) void attn_av_kernel(AvArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// A.V LDS: two V^T tiles (shared); per wave one P tile (32 rows x 128 bytes,
+// chunk c of row r at chunk c ^ (r & 7)) and the tile's alpha of each lane's
+// row (one word per lane).  Values that come from memory reach registers only
+// through LDS reads issued and waited for within one tile step, so no
+// register is written by a load still in flight across the loop.
+constexpr int kAvPB = 32 * 128, kAvAB = 64 * 4;
+
+__global__ __launch_bounds__(kAvWaves * 64) void attn_av_kernel(AvArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB + kAvWaves * (kAvPB + kAvAB)];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, hh = lane >> 5;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int qrow = blockIdx.x * kUnfRows + wave * 32 + lr;
-  const int qr = min(qrow, a.S - 1);
+  const int row0 = blockIdx.x * (kAvWaves * 32) + wave * 32;
+  const int qrow = row0 + lr;
   const RowTiles rt = row_tiles(a.txt_len, b, a.T_img);
   const int64_t Kp = (int64_t)a.nt_max * kFwdBN;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int64_t row = bh * a.S + qr;
-  const uint16_t* const prow = a.p + row * Kp;
-  const float* const arow = a.alpha + row * a.nt_max;
+  char* const pbuf = smem + 2 * kTileB + wave * kAvPB;
+  char* const abuf = smem + 2 * kTileB + kAvWaves * kAvPB + wave * kAvAB;
+
+  const int base_row = min(row0, a.S - 1);
+  const char* const pbase = (const char*)(a.p + (bh * a.S + base_row) * Kp);
+  uint32_t poff[4];  // load i, lane l: row 8i + l/8, logical chunk (l%8) ^ (row & 7)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int rr = min(row0 + r, a.S - 1) - base_row;
+    poff[i] = (uint32_t)rr * (uint32_t)(Kp * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
+  }
+  // alpha of this lane's row: scalar base at the wave's first row
+  const char* const abase = (const char*)(a.alpha + (bh * a.S + base_row) * a.nt_max);
+  const uint32_t aoff = (uint32_t)(min(qrow, a.S - 1) - base_row) * (uint32_t)(a.nt_max * 4);
+  auto load_p = [&](int t) {
+    const char* src = pbase + (int64_t)t * kFwdBN * 2;
+    const uint32_t dst = addr_of(pbuf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(src, poff[i], dst + 1024u * i);
+    dma4(abase, aoff + 4u * (uint32_t)t, addr_of(abuf));
+  };
   const uint16_t* const vt_bh = a.vt + bh * a.nt_max * kVtileElems;
+  const VtOff vo = vt_offsets(lane);
+  auto load_v = [&](int t) { load_vt(vt_bh + (int64_t)t * kVtileElems, vo, smem + (t & 1) * kTileB, wave - 4); };
+  const uint32_t vb0 = vt_base(addr_of(smem), lane);
+  // this lane's P operand: keys 16c2 + 4hh .. +3 (chunk 2c2, half hh) and
+  // 16c2 + 8 + 4hh .. +3 (chunk 2c2 + 1, half hh) of row lr
+  const uint32_t pr = addr_of(pbuf) + (uint32_t)(lr * 128 + 8 * hh);
 
   f32x16 acc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+
+  if (wave >= 4) load_v(0);
+  load_p(0);
   for (int t = 0; t < rt.nt; ++t) {
-    const float al = arow[t];
+    // V^T tile t (waves 4-7), this wave's P tile t and alpha of tile t
+    // landed; every wave is done with V^T buffer (t+1)&1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bar();
+    if (wave >= 4 && t + 1 < rt.nt) load_v(t + 1);
+    u32x2v pw[8];
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t ad = pr + (uint32_t)(16 * ((2 * c2 + j) ^ (lr & 7)));
+        asm volatile("ds_read_b64 %0, %1" : "=v"(pw[2 * c2 + j]) : "v"(ad));
+      }
+    u32x4 vf[16];
+    const uint32_t vb = vb0 + (uint32_t)((t & 1) * kTileB);
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      vf[4 * c2 + 0] = ds_b128<0 * 32 * kVtRowB>(vb ^ (uint32_t)(c2 << 5));
+      vf[4 * c2 + 1] = ds_b128<1 * 32 * kVtRowB>(vb ^ (uint32_t)(c2 << 5));
+      vf[4 * c2 + 2] = ds_b128<2 * 32 * kVtRowB>(vb ^ (uint32_t)(c2 << 5));
+      vf[4 * c2 + 3] = ds_b128<3 * 32 * kVtRowB>(vb ^ (uint32_t)(c2 << 5));
+    }
+    float al;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(al) : "v"(addr_of(abuf) + 4u * (uint32_t)lane));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(al) :: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(pw[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(vf[i]));
+    if (t + 1 < rt.nt) load_p(t + 1);  // this wave's P and alpha reads are done
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[d][r] = acc[d][r] * al;
-    const uint16_t* const vtile = vt_bh + (int64_t)t * kVtileElems;
 #pragma unroll
     for (int c2 = 0; c2 < 4; ++c2) {
-      // B operand: P^T rows 8*hh .. 8*hh+7 of chunk c2 = keys 16*c2 + 4*hh + {0..3}, 16*c2 + 8 + 4*hh + {0..3}
-      const u32x2 lo = *(const u32x2*)(prow + kFwdBN * t + 16 * c2 + 4 * hh);
-      const u32x2 hi = *(const u32x2*)(prow + kFwdBN * t + 16 * c2 + 8 + 4 * hh);
-      const u32x4 pw = {lo[0], lo[1], hi[0], hi[1]};
-      const f16x8 pf = __builtin_bit_cast(f16x8, pw);
+      const u32x4 pq = {pw[2 * c2].x, pw[2 * c2].y, pw[2 * c2 + 1].x, pw[2 * c2 + 1].y};
+      const f16x8 pf = __builtin_bit_cast(f16x8, pq);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        // A operand: V^T channel 32*d + lr, positions 8*hh .. 8*hh+7 of chunk c2 (the tile's key order)
-        const u32x4 vw = *(const u32x4*)(vtile + (32 * d + lr) * kFwdBN + 16 * c2 + 8 * hh);
-        acc[d] = mfma32h(__builtin_bit_cast(f16x8, vw), pf, acc[d]);
-      }
+      for (int d = 0; d < 4; ++d) acc[d] = mfma32h(__builtin_bit_cast(f16x8, vf[4 * c2 + d]), pf, acc[d]);
     }
   }
   // O = acc / (l * 2^-8), one RNE cast
-  const float l_div = a.l[row] * kVScale;
+  const float l_div = a.l[bh * a.S + min(qrow, a.S - 1)] * kVScale;
   if (qrow < a.S) {
     uint16_t* orow = a.o.row(b, qrow, h);
     float* frow = a.of ? a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim : nullptr;

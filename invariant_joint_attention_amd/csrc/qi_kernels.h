@@ -98,7 +98,9 @@ __global__ void v_tiles_kernel(VtileArgs a);
 // over the query rows, with Kp = 64 * nt_max key slots per row: slot 64*t + j
 // is key j of logical key tile t (slots of keys past a tile's valid count,
 // and of tiles past the row's tile count, hold the masked value).
-constexpr int kUnfRows = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kQkWaves = 8;       // score operator: waves (x 32 query rows) per workgroup
+constexpr int kSoftmaxWaves = 4;  // softmax operator
+constexpr int kAvWaves = 8;       // A.V operator
 struct QkArgs {
   View<const uint16_t> q, k;
   float* s;  // FP32 raw scores q'.k' [B][H][S][Kp] (B of this launch); masked = -inf
