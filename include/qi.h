@@ -145,6 +145,63 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
                       hipStream_t stream);
 
 /*
+ * Key-block forward and merge -- the ring-ready form of qi_joint_attn_fwd
+ * ([Kernel list], row joint_attention_fused, which is marked for Ulysses /
+ * Ring sequence parallelism; [Roadmap], "Numerical requirements": distributed
+ * execution reproduces the single-device bytes).  The keys of each row are
+ * split into blocks; every block yields a row state (acc, m, l) on its own,
+ * in any order, on any device, and qi_joint_attn_merge folds the states in
+ * the fixed block order k = 0, 1, ...:
+ *   m = max_k m_k;  alpha_k = exp2((m_k - m) c);  acc = sum_k alpha_k acc_k;
+ *   l = sum_k alpha_k l_k (both summed in ascending k);
+ *   O = bf16(acc / (l 2^-8));  LSE = (m c + log2 l) ln 2,  c = log2(e)/sqrt(128).
+ * One block holding every key gives O, LSE and O_f32 equal byte for byte to
+ * qi_joint_attn_fwd.  With several blocks the bytes are fixed by the block
+ * partition alone (not by the order, device or launch that produced each
+ * state).
+ *
+ * A block: the text keys j < txt_len[b] of every row when include_text = 1,
+ * plus the image keys T_txt + i with img_begin <= i < img_end; img_begin a
+ * multiple of 64, img_end a multiple of 64 or grid_h * grid_w (the key tiles
+ * of the whole-row forward stay whole).  The blocks passed to one merge must
+ * cover every key of every row exactly once.
+ */
+typedef struct {
+  int32_t include_text;
+  int32_t img_begin, img_end;
+} qi_key_block;
+
+/*
+ * qi_joint_attn_fwd_partial -- the forward over one key block: the row state
+ * after the block's key tiles, in the whole-row kernel's arithmetic.
+ *   q, k, v  as for qi_joint_attn_fwd.
+ *   acc      FP32 dense [B][H][S][128] output: sum_j p_j v_j 2^-8 with
+ *            p_j = exp2(s_j c - m c) (FP16 V operand of the forward).
+ *   m        FP32 dense [B][H][S] output: the block's reference max m of the
+ *            raw scores (-inf for a row without keys in the block).
+ *   l        FP32 dense [B][H][S] output: sum_j p_j (0 without keys).
+ *            m and l need 4-byte alignment only (so that stacked states of
+ *            any B*H*S can be written block by block); acc 16 bytes.
+ *   workspace  as for qi_joint_attn_fwd.
+ * QI_E_INVALID for a block outside the image range, not tile-aligned, or
+ * empty.
+ */
+int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v,
+                              qi_key_block block, float* acc, float* m, float* l,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qi_joint_attn_merge -- fold n_blocks row states in ascending block order.
+ *   acc, m, l  stacks of n_blocks states, block k at acc + k*B*H*S*128,
+ *            m + k*B*H*S, l + k*B*H*S (1 <= n_blocks <= 4096).
+ *   o        BF16 [B,S,H,128] output; lse FP32 dense [B,H,S] output;
+ *            o_f32 nullable FP32 dense [B,S,H,128] output.
+ */
+int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc,
+                        const float* m, const float* l, qi_bshd o, float* lse, float* o_f32,
+                        hipStream_t stream);
+
+/*
  * Unfused forward -- the three attention operators of [Kernel list], rows
  * joint_attn_qk_gemm, joint_attn_softmax and joint_attn_av_gemm, whose
  * composition qk_gemm -> softmax -> av_gemm gives O, LSE (and O_f32) equal

@@ -22,7 +22,8 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
           5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
 
 # every entry point declared in include/qi.h
-SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_key_slots",
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial",
+           "qi_joint_attn_merge", "qi_joint_attn_key_slots",
            "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
            "qi_joint_attn_bwd", "qi_last_error", "qi_strict_probe", "qi_trace")
 
@@ -35,6 +36,10 @@ class QiError(RuntimeError):
 
 class QiBshd(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("sb", ctypes.c_int64), ("ss", ctypes.c_int64), ("sh", ctypes.c_int64)]
+
+
+class QiKeyBlock(ctypes.Structure):
+    _fields_ = [("include_text", ctypes.c_int32), ("img_begin", ctypes.c_int32), ("img_end", ctypes.c_int32)]
 
 
 class QiGeom(ctypes.Structure):
@@ -60,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd_workspace.argtypes = [G]
         L.qi_joint_attn_fwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
+        L.qi_joint_attn_fwd_partial.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, ctypes.c_size_t, S]
+        L.qi_joint_attn_merge.argtypes = [G, ctypes.c_int32, P, P, P, QiBshd, P, P, S]
         L.qi_joint_attn_key_slots.argtypes = [G]
         L.qi_joint_attn_key_slots.restype = ctypes.c_int64
         L.qi_joint_attn_qk_gemm.argtypes = [G, QiBshd, QiBshd, P, S]
@@ -72,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.qi_last_error.restype = ctypes.c_char_p
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
-        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
+        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
+                     "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
                      "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_strict_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -153,6 +161,35 @@ def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None, wo
     _check(lib().qi_joint_attn_fwd(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
                                    _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream()))
+    return out, lse
+
+
+def joint_attn_fwd_partial(q, k, v, geom: Geometry, include_text: bool, img_begin: int, img_end: int,
+                           acc=None, m=None, l=None, workspace=None):
+    """Row state of one key block: (acc FP32 [B,H,S,128], m FP32 [B,H,S],
+    l FP32 [B,H,S]); acc holds sum_j p_j v_j 2^-8."""
+    B, H, S = geom.B, geom.H, geom.S
+    acc = _empty((B, H, S, HEAD_DIM), torch.float32, q) if acc is None else acc
+    m = _empty((B, H, S), torch.float32, q) if m is None else m
+    l = _empty((B, H, S), torch.float32, q) if l is None else l
+    if workspace is None:
+        workspace = _empty((max(1, fwd_workspace_bytes(geom)),), torch.uint8, q)
+    blk = QiKeyBlock(int(bool(include_text)), int(img_begin), int(img_end))
+    _check(lib().qi_joint_attn_fwd_partial(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), blk, _ptr(acc), _ptr(m), _ptr(l),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return acc, m, l
+
+
+def joint_attn_merge(acc, m, l, geom: Geometry, out=None, lse=None, out_f32=None):
+    """Fold stacked row states (acc [n,B,H,S,128], m and l [n,B,H,S]) in
+    ascending block order; returns (O BF16 [B,S,H,128], LSE FP32 [B,H,S])."""
+    n = acc.shape[0]
+    if out is None:
+        out = torch.empty((geom.B, geom.S, geom.H, HEAD_DIM), dtype=torch.bfloat16, device=acc.device)
+    if lse is None:
+        lse = _empty((geom.B, geom.H, geom.S), torch.float32, acc)
+    _check(lib().qi_joint_attn_merge(geom.ptr(), int(n), _ptr(acc), _ptr(m), _ptr(l), _bshd(out), _ptr(lse),
+                                     _ptr(out_f32), _stream()))
     return out, lse
 
 

@@ -107,9 +107,9 @@ int check_view(const qi_geom* g, const qi_bshd& v, int elsize, bool output, cons
 }
 
 int check_dense(const void* p, int64_t bytes, bool output, const char* name, std::vector<Extent>& ext,
-                bool nullable = false) {
+                bool nullable = false, int align = 16) {
   if (!p) return nullable ? QI_OK : fail(QI_E_INVALID, "%s is null", name);
-  if ((uintptr_t)p % 16) return fail(QI_E_ALIGN, "%s is not 16-byte aligned", name);
+  if ((uintptr_t)p % align) return fail(QI_E_ALIGN, "%s is not %d-byte aligned", name, align);
   ext.push_back({name, (uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, output});
   return QI_OK;
 }
@@ -258,6 +258,66 @@ BwdLayout bwd_layout(const qi_geom* g) {
   return L;
 }
 
+// One forward call: the V tile pass and the attention kernel per batch chunk.
+// With blk the partial kernel runs over that key block and writes the row
+// state (acc, m, l) instead of O and LSE.
+int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_p, float* lse, float* o_f32,
+               uint16_t* vt, const qi_key_block* blk, float* pacc, float* pm, float* pl, hipStream_t stream) {
+  int rc;
+  const int64_t S = seq_len(geom);
+  // vt: FP16 V^T key tiles [B][H][nt_max][128][64] in the workspace
+  const int nt_max = fwd_nt_max(geom);
+  const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    FwdArgs a;
+    a.q = view_of<const uint16_t>(q, b0);
+    a.k = view_of<const uint16_t>(k, b0);
+    a.vt = vt + (int64_t)b0 * geom->H * nt_max * kVtileElems;
+    a.o = o_p ? view_of<uint16_t>(*o_p, b0) : View<uint16_t>{nullptr, 0, 0, 0};
+    a.lse = lse ? lse + (int64_t)b0 * geom->H * S : nullptr;
+    a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
+    const int64_t r0 = (int64_t)b0 * geom->H * S;
+    a.blk_text = blk ? blk->include_text : 1;
+    a.blk_img_t0 = blk ? blk->img_begin / kFwdBN : 0;
+    a.blk_img_t1 = blk ? (int)ceil_div(blk->img_end, kFwdBN) : 0;
+    a.pacc = pacc ? pacc + r0 * kHeadDim : nullptr;
+    a.pm = pm ? pm + r0 : nullptr;
+    a.pl = pl ? pl + r0 : nullptr;
+    a.B = nb;
+    a.S = (int)S;
+    a.H = geom->H;
+    a.T_txt = geom->T_txt;
+    a.T_img = geom->grid_h * geom->grid_w;
+    a.nt_max = nt_max;
+    a.n_qtiles = (int)ceil_div(S, rows_per_wg);
+    a.xcd_remap = ((nb * geom->H) % 8) == 0;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+
+    VtileArgs c;
+    c.v = view_of<const uint16_t>(v, b0);
+    c.out = const_cast<uint16_t*>(a.vt);
+    c.H = geom->H;
+    c.T_txt = geom->T_txt;
+    c.T_img = a.T_img;
+    c.nt_max = nt_max;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
+    hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
+                       c);
+    if ((rc = launched("v_tiles_kernel"))) return rc;
+
+    const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
+    if (blk) {
+      hipLaunchKernelGGL(attn_fwd_partial_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
+      if ((rc = launched("attn_fwd_partial_kernel"))) return rc;
+    } else {
+      hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
+      if ((rc = launched("attn_fwd_kernel"))) return rc;
+    }
+  }
+  return QI_OK;
+}
+
 int launch_prologue(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd y, float* yf, hipStream_t st) {
   PrologueArgs a;
   a.x = view_of<const uint16_t>(x, 0);
@@ -370,45 +430,74 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
     return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
 
-  uint16_t* vt = (uint16_t*)workspace;  // FP16 V^T key tiles [B][H][nt_max][128][64]
-  const int nt_max = fwd_nt_max(geom);
-  const int rows_per_wg = kFwdWaves * kFwdRowsPerWave;
-  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
-    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
-    FwdArgs a;
-    a.q = view_of<const uint16_t>(q, b0);
-    a.k = view_of<const uint16_t>(k, b0);
-    a.vt = vt + (int64_t)b0 * geom->H * nt_max * kVtileElems;
-    a.o = view_of<uint16_t>(o, b0);
-    a.lse = lse + (int64_t)b0 * geom->H * S;
-    a.of = o_f32 ? o_f32 + (int64_t)b0 * S * geom->H * kHeadDim : nullptr;
-    a.B = nb;
-    a.S = (int)S;
-    a.H = geom->H;
-    a.T_txt = geom->T_txt;
-    a.T_img = geom->grid_h * geom->grid_w;
-    a.nt_max = nt_max;
-    a.n_qtiles = (int)ceil_div(S, rows_per_wg);
-    a.xcd_remap = ((nb * geom->H) % 8) == 0;
-    for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+  return launch_fwd(geom, q, k, v, &o, lse, o_f32, (uint16_t*)workspace, nullptr, nullptr, nullptr, nullptr, stream);
+}
 
-    VtileArgs c;
-    c.v = view_of<const uint16_t>(v, b0);
-    c.out = const_cast<uint16_t*>(a.vt);
-    c.H = geom->H;
-    c.T_txt = geom->T_txt;
-    c.T_img = a.T_img;
-    c.nt_max = nt_max;
-    for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
-    hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
-                       c);
-    if ((rc = launched("v_tiles_kernel"))) return rc;
+int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_key_block blk, float* acc,
+                              float* m, float* l, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  const int64_t S = seq_len(geom), T_img = (int64_t)geom->grid_h * geom->grid_w;
+  if (blk.include_text != 0 && blk.include_text != 1)
+    return fail(QI_E_INVALID, "include_text=%d must be 0 or 1", blk.include_text);
+  if (blk.img_begin < 0 || blk.img_begin > blk.img_end || blk.img_end > T_img)
+    return fail(QI_E_INVALID, "image key range [%d, %d) outside [0, %lld]", blk.img_begin, blk.img_end,
+                (long long)T_img);
+  if (blk.img_begin % kFwdBN || (blk.img_end % kFwdBN && blk.img_end != T_img))
+    return fail(QI_E_INVALID, "image key range [%d, %d) is not aligned to the 64-key tiles", blk.img_begin,
+                blk.img_end);
+  if (!blk.include_text && blk.img_begin == blk.img_end) return fail(QI_E_INVALID, "empty key block");
+  std::vector<Extent> ext;
+  const int64_t rows = (int64_t)geom->B * geom->H * S;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_dense(acc, rows * kHeadDim * 4, true, "acc", ext))) return rc;
+  if ((rc = check_dense(m, rows * 4, true, "m", ext, false, 4))) return rc;  // one word per row
+  if ((rc = check_dense(l, rows * 4, true, "l", ext, false, 4))) return rc;
+  const size_t ws_need = fwd_workspace_bytes(geom);
+  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < ws_need)
+    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
+  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
+  if ((rc = check_alias(ext))) return rc;
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if ((rc = current_device_gate())) return rc;
+  return launch_fwd(geom, q, k, v, nullptr, nullptr, nullptr, (uint16_t*)workspace, &blk, acc, m, l, stream);
+}
 
-    const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
-    if ((rc = launched("attn_fwd_kernel"))) return rc;
-  }
-  return QI_OK;
+int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc, const float* m, const float* l,
+                        qi_bshd o, float* lse, float* o_f32, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  if (n_blocks < 1 || n_blocks > kMaxMergeBlocks)
+    return fail(QI_E_INVALID, "n_blocks=%d outside [1, %d]", n_blocks, kMaxMergeBlocks);
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t rows = (int64_t)geom->B * geom->H * S;
+  if ((rc = check_dense(acc, n_blocks * rows * kHeadDim * 4, false, "acc", ext))) return rc;
+  if ((rc = check_dense(m, n_blocks * rows * 4, false, "m", ext, false, 4))) return rc;
+  if ((rc = check_dense(l, n_blocks * rows * 4, false, "l", ext, false, 4))) return rc;
+  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+  if ((rc = check_dense(lse, rows * 4, true, "lse", ext))) return rc;
+  if ((rc = check_dense(o_f32, rows * kHeadDim * 4, true, "o_f32", ext, true))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  MergeArgs a;
+  a.acc = acc;
+  a.m = m;
+  a.l = l;
+  a.rows = rows;
+  a.o = view_of<uint16_t>(o, 0);
+  a.lse = lse;
+  a.of = o_f32;
+  a.n = n_blocks;
+  a.S = (int)S;
+  a.H = geom->H;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)ceil_div(rows, 8)), dim3(256), 0, stream, a);
+  return launched("attn_merge_kernel");
 }
 
 int64_t qi_joint_attn_key_slots(const qi_geom* geom) {
@@ -640,7 +729,7 @@ const char* qi_trace(void) {
     snprintf(buf, sizeof buf,
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\",\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\",\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\",\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
              "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","

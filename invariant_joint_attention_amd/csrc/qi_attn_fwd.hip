@@ -254,7 +254,12 @@ __device__ __forceinline__ void sm_block(St& st, int cur_valid, int hh) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) {
+// The forward over all key tiles of each row (kPartial = false), or over the
+// tiles of one key block with the row state (acc, reference max, row sum)
+// written out instead of O (kPartial = true).  A block's tiles are processed
+// exactly as the whole row's: same order, same arithmetic per tile.
+template <bool kPartial>
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
   __shared__ __attribute__((aligned(1024))) char smem[(kKRing + kVRing) * kTileB];
 
   const int lane = threadIdx.x & 63;
@@ -292,7 +297,32 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   st.l = 0.f;
 
   const int ntxt = (L + kFwdBN - 1) / kFwdBN;
-  const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
+  // Tiles processed, in key order: u < ntb are text tiles u; the others are
+  // image tiles from t_img0 on (all of them unless kPartial).
+  const int nimg = (a.T_img + kFwdBN - 1) / kFwdBN;
+  const int ntb = kPartial ? (a.blk_text ? ntxt : 0) : ntxt;
+  const int t_img0 = kPartial ? min(a.blk_img_t0, nimg) : 0;
+  const int nt = kPartial ? ntb + max(0, min(a.blk_img_t1, nimg) - t_img0) : ntxt + nimg;
+  auto tix = [&](int u) {
+    if constexpr (kPartial)
+      return u < ntb ? u : ntxt + t_img0 + (u - ntb);
+    else
+      return u;
+  };
+  if constexpr (kPartial) {
+    if (nt == 0) {  // no key of this row in the block (uniform over the workgroup)
+      if (qrow < a.S) {
+        const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
+        float* prow = a.pacc + row * kHeadDim;
+        for (int c = 4 * hh; c < kHeadDim; c += 8) *(f32x4*)(prow + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (hh == 0) {
+          a.pm[row] = -INFINITY;
+          a.pl[row] = 0.f;
+        }
+      }
+      return;
+    }
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
   auto kbuf = [&](int j) { return smem + (j % kKRing) * kTileB; };
   auto vbuf = [&](int j) { return smem + kVRingOfs + (j % kVRing) * kTileB; };
@@ -300,7 +330,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   auto vofs = [&](int j) { return (uint32_t)((j % kVRing) * kTileB); };
   auto valid_of = [&](int j) {
     int k0, nv;
-    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    tile_bounds(tix(j), ntxt, L, a.T_txt, a.T_img, k0, nv);
     return nv;
   };
   // Group 0 loads whole K tiles, group 1 whole V^T tiles: wave `sub` of a
@@ -311,7 +341,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   const RowOff ko = row_offsets(a.k.ss, lane);
   auto load_k = [&](int j) {
     int k0, nv;
-    tile_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
+    tile_bounds(tix(j), ntxt, L, a.T_txt, a.T_img, k0, nv);
     const int r0 = 16 * sub;
     const uint32_t la = addr_of(kbuf(j) + r0 * kRowB);
     if (nv >= r0 + 16) {
@@ -333,7 +363,7 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   };
   const VtOff vo = vt_offsets(lane);
   const uint16_t* const vt_bh = a.vt + ((int64_t)b * a.H + h) * a.nt_max * kVtileElems;
-  auto load_v = [&](int j) { load_vt(vt_bh + (int64_t)j * kVtileElems, vo, vbuf(j), sub); };
+  auto load_v = [&](int j) { load_vt(vt_bh + (int64_t)tix(j) * kVtileElems, vo, vbuf(j), sub); };
 
   Addr ad;
   {
@@ -397,10 +427,29 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
     mm_block<true, true>(st, fr, am);
   }
 
-  // ---- epilogue: O = acc / l, one RNE cast; LSE in natural log
+  // ---- epilogue
   const uint32_t lu = __float_as_uint(st.l);
   const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if constexpr (kPartial) {
+    // the row state: acc (sum_j p_j v_j 2^-8, FP32), reference max, row sum
+    if (qrow < a.S) {
+      const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
+      float* prow = a.pacc + row * kHeadDim;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(f32x4*)(prow + 32 * d + 8 * g4 + 4 * hh) =
+              f32x4{st.acc[d][4 * g4], st.acc[d][4 * g4 + 1], st.acc[d][4 * g4 + 2], st.acc[d][4 * g4 + 3]};
+      if (hh == 0) {
+        a.pm[row] = st.m_used;
+        a.pl[row] = l_tot;
+      }
+    }
+    return;
+  }
+  // O = acc / l, one RNE cast; LSE in natural log
   // acc holds sum_j p_j v_j 2^-8: divide by l * 2^-8 (exact scaling)
   const float l_div = l_tot * kVScale;
   if (qrow < a.S) {
@@ -424,6 +473,9 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) 
   }
 }
 
+
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) { attn_fwd_body<false>(a); }
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_partial_kernel(FwdArgs a) { attn_fwd_body<true>(a); }
 
 // V -> FP16 V^T key tiles.  One workgroup per (logical key tile t, h, b):
 // the tile's valid key rows are staged in LDS as BF16, then written out as
@@ -463,6 +515,44 @@ __global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {
     const u32x4 o = {pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7])};
     *(u32x4*)(out + d * kFwdBN + 8 * j) = o;
   }
+}
+
+// Merge of key-block row states in the fixed block order k = 0, 1, ...:
+// m = max_k m_k; alpha_k = exp2((m_k - m) c); acc = alpha_0 acc_0 + alpha_1
+// acc_1 + ...; l likewise; then the forward's epilogue, O = acc / (l 2^-8)
+// and LSE = (m c + log2 l) ln 2.  With one block alpha_0 = exp2(0) = 1 and
+// the result is the whole-row forward's, bit for bit.  A block without keys
+// for a row (m = -inf, acc = l = 0) gets alpha = 0.  32 lanes per row, 4
+// channels per lane.
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= a.rows) return;
+  const int c0 = 4 * (threadIdx.x & 31);
+  float m = -INFINITY;
+  for (int k = 0; k < a.n; ++k) m = fmaxf(m, a.m[k * a.rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int k = 0; k < a.n; ++k) {
+    const float al = __builtin_amdgcn_exp2f((a.m[k * a.rows + row] - m) * kC);
+    const f32x4 x = *(const f32x4*)(a.acc + (k * a.rows + row) * kHeadDim + c0);
+    const float lk = a.l[k * a.rows + row];
+    if (k == 0) {
+      for (int e = 0; e < 4; ++e) acc[e] = al * x[e];
+      l = al * lk;
+    } else {
+      for (int e = 0; e < 4; ++e) acc[e] = acc[e] + al * x[e];
+      l = l + al * lk;
+    }
+  }
+  const float l_div = l * kVScale;
+  const int64_t bh = row / a.S;
+  const int qrow = (int)(row - bh * a.S);
+  const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
+  const float o0 = acc[0] / l_div, o1 = acc[1] / l_div, o2 = acc[2] / l_div, o3 = acc[3] / l_div;
+  const u32x2 ov = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+  *(u32x2*)(a.o.row(b, qrow, h) + c0) = ov;
+  if (a.of) *(f32x4*)(a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim + c0) = f32x4{o0, o1, o2, o3};
+  if (c0 == 0) a.lse[row] = (m * kC + log2f(l)) * kLn2;
 }
 
 }  // namespace qi

@@ -55,6 +55,27 @@ struct FwdArgs {
   int n_qtiles;   // ceil(S / rows per workgroup)
   int xcd_remap;  // 1: group the query tiles of a (b, h) on one XCD
   int txt_len[kMaxBatchPerLaunch];
+  // partial forward only: the key block (text tiles when blk_text; image
+  // tiles blk_img_t0 <= t < blk_img_t1) and the row-state outputs
+  int blk_text, blk_img_t0, blk_img_t1;
+  float* pacc;  // [B][H][S][128]: sum_j p_j v_j 2^-8 (B of this launch)
+  float* pm;    // [B][H][S]: reference max of the raw scores
+  float* pl;    // [B][H][S]: row sum of p
+};
+
+constexpr int kMaxMergeBlocks = 4096;  // key blocks one merge call folds
+
+// Fixed-order merge of the row states of n key blocks (block k of every
+// array at offset k * blk_stride elements, rows at 1 element / 128 for acc).
+struct MergeArgs {
+  const float* acc;  // [n][rows][128]
+  const float* m;    // [n][rows]
+  const float* l;    // [n][rows]
+  int64_t rows;      // B * H * S
+  View<uint16_t> o;
+  float* lse;  // [B][H][S]
+  float* of;   // nullable dense [B,S,H,128]
+  int n, S, H;
 };
 
 // Backward attention.
@@ -79,6 +100,8 @@ __global__ void qknorm_rope_fwd_kernel(PrologueArgs a);
 __global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
 __global__ void dgain_fold_kernel(DgainFoldArgs a);
 __global__ void attn_fwd_kernel(FwdArgs a);
+__global__ void attn_fwd_partial_kernel(FwdArgs a);
+__global__ void attn_merge_kernel(MergeArgs a);
 
 // V -> FP16 (v * 2^-8) conversion pass of the forward: writes each logical
 // key tile of 64 keys transposed, as 128 channel rows of 64 keys, the keys of

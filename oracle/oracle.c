@@ -246,14 +246,24 @@ void oracle_qknorm_rope(int B, int S, int H, int T_txt, int gh, int gw,
  * are j < L and T_txt <= j < S.  Per (batch, head) slice; q, k, v are the
  * dense [S][128] rows of that slice.
  * ---------------------------------------------------------------------- */
-static int key_valid(int j, int T_txt, int L) { return j < L || j >= T_txt; }
+/* A row's key set: the text keys j < L and the image keys T_txt + i with
+ * img_lo <= i < img_hi.  The attention of a row uses all its image keys
+ * (img_lo = 0, img_hi = S - T_txt); a key block of a split forward uses a
+ * range of them, with or without the text keys. */
+typedef struct { int T_txt, L, img_lo, img_hi; } keyset;
+static keyset all_keys(int S, int T_txt, int L) {
+  keyset ks = {T_txt, L, 0, S - T_txt};
+  return ks;
+}
+static int key_valid(int j, keyset ks) {
+  return j < ks.L || (j >= ks.T_txt + ks.img_lo && j < ks.T_txt + ks.img_hi);
+}
 static real softmax_scale(void) { return (real)(1.0 / sqrt((double)HD)); }
 
-static void scores_row(int S, int T_txt, int L, const real* qi, const real* k,
-                       real* srow) {
+static void scores_row(int S, keyset ks, const real* qi, const real* k, real* srow) {
   real sc = softmax_scale();
   for (int j = 0; j < S; ++j) {
-    if (!key_valid(j, T_txt, L)) { srow[j] = 0; continue; }
+    if (!key_valid(j, ks)) { srow[j] = 0; continue; }
     const real* kj = k + (int64_t)j * HD;
     real dot = 0;
     for (int c = 0; c < HD; ++c) {
@@ -266,14 +276,13 @@ static void scores_row(int S, int T_txt, int L, const real* qi, const real* k,
 
 /* Softmax of one score row over the valid keys; returns the row max and
  * fills p (masked entries exactly 0) and *lse = m + log(sum exp(s - m)). */
-static void softmax_row(int S, int T_txt, int L, const real* srow, real* p,
-                        real* lse) {
+static void softmax_row(int S, keyset ks, const real* srow, real* p, real* lse) {
   real m = -INFINITY;
   for (int j = 0; j < S; ++j)
-    if (key_valid(j, T_txt, L) && srow[j] > m) m = srow[j];
+    if (key_valid(j, ks) && srow[j] > m) m = srow[j];
   real l = 0;
   for (int j = 0; j < S; ++j) {
-    if (!key_valid(j, T_txt, L)) { p[j] = 0; continue; }
+    if (!key_valid(j, ks)) { p[j] = 0; continue; }
     p[j] = exp(srow[j] - m);
     l = l + p[j];
   }
@@ -281,21 +290,22 @@ static void softmax_row(int S, int T_txt, int L, const real* srow, real* p,
   *lse = m + log(l);
 }
 
-/* Forward for query rows [s0, s1): o [s1-s0][128] pre-cast, lse [s1-s0]. */
-void oracle_attn_fwd_bh(int S, int T_txt, int L, const real* q, const real* k,
-                        const real* v, int s0, int s1, real* o, real* lse) {
+/* Forward of query rows [s0, s1) over the key set ks: o [s1-s0][128]
+ * pre-cast, lse [s1-s0]. */
+static void attn_fwd_keys(int S, keyset ks, const real* q, const real* k,
+                          const real* v, int s0, int s1, real* o, real* lse) {
 #pragma omp parallel
   {
     real* srow = (real*)malloc(sizeof(real) * (size_t)S);
     real* p = (real*)malloc(sizeof(real) * (size_t)S);
 #pragma omp for schedule(static)
     for (int i = s0; i < s1; ++i) {
-      scores_row(S, T_txt, L, q + (int64_t)i * HD, k, srow);
-      softmax_row(S, T_txt, L, srow, p, &lse[i - s0]);
+      scores_row(S, ks, q + (int64_t)i * HD, k, srow);
+      softmax_row(S, ks, srow, p, &lse[i - s0]);
       real acc[HD];
       for (int c = 0; c < HD; ++c) acc[c] = 0;
       for (int j = 0; j < S; ++j) {
-        if (!key_valid(j, T_txt, L)) continue;
+        if (!key_valid(j, ks)) continue;
         const real* vj = v + (int64_t)j * HD;
         for (int c = 0; c < HD; ++c) {
           real pr = p[j] * vj[c];
@@ -309,6 +319,24 @@ void oracle_attn_fwd_bh(int S, int T_txt, int L, const real* q, const real* k,
   }
 }
 
+/* Forward for query rows [s0, s1) over all keys of the row. */
+void oracle_attn_fwd_bh(int S, int T_txt, int L, const real* q, const real* k,
+                        const real* v, int s0, int s1, real* o, real* lse) {
+  attn_fwd_keys(S, all_keys(S, T_txt, L), q, k, v, s0, s1, o, lse);
+}
+
+/* Forward over one key block [Kernel list, row joint_attention_fused: the
+ * fused operator is marked for ring sequence parallelism, where each device
+ * holds a block of the keys]: the text keys j < L when with_text, and the
+ * image keys T_txt + i with img_lo <= i < img_hi.  o and lse describe
+ * attention restricted to those keys. */
+void oracle_attn_fwd_block_bh(int S, int T_txt, int L, int with_text, int img_lo,
+                              int img_hi, const real* q, const real* k, const real* v,
+                              int s0, int s1, real* o, real* lse) {
+  keyset ks = {T_txt, with_text ? L : 0, img_lo, img_hi};
+  attn_fwd_keys(S, ks, q, k, v, s0, s1, o, lse);
+}
+
 /* The three attention operators one at a time [Kernel list, rows
  * joint_attn_qk_gemm, joint_attn_softmax, joint_attn_av_gemm], for checking
  * each unfused operator on its own.
@@ -318,7 +346,7 @@ void oracle_attn_scores_bh(int S, int T_txt, int L, const real* q, const real* k
                            int s0, int s1, real* s) {
 #pragma omp parallel for schedule(static)
   for (int i = s0; i < s1; ++i)
-    scores_row(S, T_txt, L, q + (int64_t)i * HD, k, s + (int64_t)(i - s0) * S);
+    scores_row(S, all_keys(S, T_txt, L), q + (int64_t)i * HD, k, s + (int64_t)(i - s0) * S);
 }
 
 /* Softmax over the valid keys of n rows of scaled scores [n][S]: p [n][S]
@@ -327,7 +355,7 @@ void oracle_attn_softmax_rows(int n, int S, int T_txt, int L, const real* s, rea
                               real* lse) {
 #pragma omp parallel for schedule(static)
   for (int i = 0; i < n; ++i)
-    softmax_row(S, T_txt, L, s + (int64_t)i * S, p + (int64_t)i * S, &lse[i]);
+    softmax_row(S, all_keys(S, T_txt, L), s + (int64_t)i * S, p + (int64_t)i * S, &lse[i]);
 }
 
 /* The A.V step of the online softmax [Kernel list, row joint_attn_av_gemm;
@@ -380,6 +408,7 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
   real* dS = (real*)malloc(sizeof(real) * (size_t)S * S);
   if (!P || !dS) { free(P); free(dS); return 1; }
   real sc = softmax_scale();
+  const keyset ks = all_keys(S, T_txt, L);
 #pragma omp parallel
   {
     real* srow = (real*)malloc(sizeof(real) * (size_t)S);
@@ -387,12 +416,12 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
     for (int i = 0; i < S; ++i) {
       real lse;
       real* p = P + (int64_t)i * S;
-      scores_row(S, T_txt, L, q + (int64_t)i * HD, k, srow);
-      softmax_row(S, T_txt, L, srow, p, &lse);
+      scores_row(S, ks, q + (int64_t)i * HD, k, srow);
+      softmax_row(S, ks, srow, p, &lse);
       real oi[HD];
       for (int c = 0; c < HD; ++c) oi[c] = 0;
       for (int j = 0; j < S; ++j) {
-        if (!key_valid(j, T_txt, L)) continue;
+        if (!key_valid(j, ks)) continue;
         for (int c = 0; c < HD; ++c) {
           real pr = p[j] * v[(int64_t)j * HD + c];
           oi[c] = oi[c] + pr;
@@ -406,7 +435,7 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
       }
       real* ds = dS + (int64_t)i * S;
       for (int j = 0; j < S; ++j) {
-        if (!key_valid(j, T_txt, L)) { ds[j] = 0; continue; }
+        if (!key_valid(j, ks)) { ds[j] = 0; continue; }
         real dp = 0;
         for (int c = 0; c < HD; ++c) {
           real pr = g[c] * v[(int64_t)j * HD + c];
@@ -417,7 +446,7 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
       for (int c = 0; c < HD; ++c) {
         real acc = 0;
         for (int j = 0; j < S; ++j) {
-          if (!key_valid(j, T_txt, L)) continue;
+          if (!key_valid(j, ks)) continue;
           real pr = ds[j] * k[(int64_t)j * HD + c];
           acc = acc + pr;
         }
@@ -430,7 +459,7 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
   for (int j = 0; j < S; ++j) {
     real* dkj = dk + (int64_t)j * HD;
     real* dvj = dv + (int64_t)j * HD;
-    if (!key_valid(j, T_txt, L)) {
+    if (!key_valid(j, ks)) {
       for (int c = 0; c < HD; ++c) { dkj[c] = 0; dvj[c] = 0; }
       continue;
     }

@@ -155,6 +155,22 @@ class Oracle:
                                     _ptr(lse, self.creal))
         return o, lse
 
+    def attn_fwd_block_bh(self, q, k, v, T_txt, L, with_text, img_lo, img_hi, s0=0, s1=None):
+        """One (batch, head) slice over one key block: the text keys j < L
+        (when with_text) and the image keys T_txt + i, img_lo <= i < img_hi.
+        Rows [s0, s1).  Returns o, lse of attention restricted to the block."""
+        q, k, v = self._r(q), self._r(k), self._r(v)
+        S = q.shape[0]
+        s1 = S if s1 is None else s1
+        o = np.empty((s1 - s0, HD), dtype=self.dtype)
+        lse = np.empty((s1 - s0,), dtype=self.dtype)
+        self.lib.oracle_attn_fwd_block_bh(ctypes.c_int(S), ctypes.c_int(T_txt), ctypes.c_int(L),
+                                          ctypes.c_int(int(bool(with_text))), ctypes.c_int(img_lo),
+                                          ctypes.c_int(img_hi), _ptr(q, self.creal), _ptr(k, self.creal),
+                                          _ptr(v, self.creal), ctypes.c_int(s0), ctypes.c_int(s1),
+                                          _ptr(o, self.creal), _ptr(lse, self.creal))
+        return o, lse
+
     def attn_fwd(self, q, k, v, txt_len, T_txt, heads=None):
         """q,k,v [B,S,H,128].  Returns o [B,S,H,128] and lse [B,H,S].
 

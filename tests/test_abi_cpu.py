@@ -248,3 +248,52 @@ def test_unfused_operators_validation():
     assert av(ws_ptr=region(9) + 16) == code("QI_E_ALIGN")
     assert av(o=fake_bshd(region(5), g.B, g.S, g.H)) == code("QI_E_ALIAS")
     assert av(of=region(7)) == code("QI_E_ALIAS")
+
+
+def test_block_forward_and_merge_validation():
+    """Key-block forward and merge: block ranges, outputs, workspace and
+    n_blocks are checked before any launch."""
+    g = geom()  # T_img = 16
+    L = qi.lib()
+    q = fake_bshd(region(0), g.B, g.S, g.H)
+    k = fake_bshd(region(1), g.B, g.S, g.H)
+    v = fake_bshd(region(2), g.B, g.S, g.H)
+    ws = L.qi_joint_attn_fwd_workspace(g.ptr())
+
+    def part(blk=(1, 0, 16), acc=region(4), m=region(5), l=region(6), ws_ptr=region(9), ws_bytes=ws):
+        return L.qi_joint_attn_fwd_partial(g.ptr(), q, k, v, qi.QiKeyBlock(*blk), acc, m, l, ws_ptr, ws_bytes, None)
+
+    assert part() == code("QI_E_UNSUPPORTED")  # valid: stops at the device gate
+    assert part(blk=(1, 0, 0)) == code("QI_E_UNSUPPORTED")  # text keys only
+    assert part(blk=(0, 0, 16)) == code("QI_E_UNSUPPORTED")  # image keys only
+    assert part(blk=(0, 0, 0)) == code("QI_E_INVALID")  # empty
+    assert part(blk=(2, 0, 16)) == code("QI_E_INVALID")
+    assert part(blk=(1, 0, 17)) == code("QI_E_INVALID")  # past the image keys
+    assert part(blk=(1, 8, 16)) == code("QI_E_INVALID")  # not tile-aligned
+    assert part(blk=(1, 16, 8)) == code("QI_E_INVALID")
+    assert part(acc=None) == code("QI_E_INVALID")
+    assert part(m=region(5) + 2) == code("QI_E_ALIGN")
+    assert part(m=region(5) + 4) == code("QI_E_UNSUPPORTED")  # one word per row: 4-byte alignment
+    assert part(acc=region(4) + 4) == code("QI_E_ALIGN")
+    assert part(l=region(5)) == code("QI_E_ALIAS")
+    assert part(acc=region(1)) == code("QI_E_ALIAS")
+    assert part(ws_ptr=None) == code("QI_E_WORKSPACE")
+    assert part(ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    g2 = geom(grid_h=16, grid_w=9)  # T_img = 144: a block may end at T_img
+    assert L.qi_joint_attn_fwd_partial(g2.ptr(), fake_bshd(region(0), g2.B, g2.S, g2.H),
+                                       fake_bshd(region(1), g2.B, g2.S, g2.H), fake_bshd(region(2), g2.B, g2.S, g2.H),
+                                       qi.QiKeyBlock(0, 128, 144), region(4), region(5), region(6), region(9),
+                                       L.qi_joint_attn_fwd_workspace(g2.ptr()), None) == code("QI_E_UNSUPPORTED")
+
+    o = fake_bshd(region(3), g.B, g.S, g.H)
+
+    def merge(n=2, acc=region(4), m=region(5), l=region(6), o=o, lse=region(7), of=None):
+        return L.qi_joint_attn_merge(g.ptr(), n, acc, m, l, o, lse, of, None)
+
+    assert merge() == code("QI_E_UNSUPPORTED")
+    assert merge(n=0) == code("QI_E_INVALID")
+    assert merge(n=4097) == code("QI_E_INVALID")
+    assert merge(m=None) == code("QI_E_INVALID")
+    assert merge(lse=region(5)) == code("QI_E_ALIAS")
+    assert merge(o=fake_bshd(region(4), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    assert merge(of=region(6) + 16) == code("QI_E_ALIAS")

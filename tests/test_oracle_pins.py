@@ -580,3 +580,37 @@ def test_operator_av_recurrence(o64, shape):
         w_t = np.prod(ar[:, t + 1:len(tiles)], axis=1)
         closed += w_t[:, None] * (Pr[:, t, :len(keys)] @ v[keys])
     assert np.abs(o - closed / lr[:, None]).max() < 1e-12
+
+
+BLOCK_CASES = [  # (T_txt, L, h, w, with_text, img_lo, img_hi)
+    (8, 5, 4, 4, True, 0, 0),
+    (8, 5, 4, 4, False, 0, 16),
+    (70, 67, 13, 11, True, 64, 128),
+    (70, 67, 13, 11, False, 128, 143),
+    (3, 0, 5, 5, True, 0, 25),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES)
+def test_block_attention_matches_sdpa(o64, case):
+    """Attention restricted to one key block equals torch SDPA with the
+    block's boolean key mask; rows of a block without keys are not asked
+    for.  The full block (text + all image keys) equals the plain forward."""
+    T, L, h, w, with_text, lo, hi = case
+    S = T + h * w
+    rng = _rng(13)
+    q, k, v = (rng.standard_normal((S, HD)) for _ in range(3))
+    keys = [j for j in range(S) if (with_text and j < L) or (T + lo <= j < T + hi)]
+    if not keys:
+        pytest.skip("block without keys")
+    mask = torch.zeros(S, dtype=torch.bool)
+    mask[keys] = True
+    qt, kt, vt = (torch.from_numpy(t)[None] for t in (q, k, v))
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None, :].expand(1, S, S))[0].numpy()
+    sc = (q @ k.T) / math.sqrt(HD)
+    ref_lse = logsumexp(np.where(mask.numpy()[None, :], sc, -np.inf), axis=-1)
+    o, lse = o64.attn_fwd_block_bh(q, k, v, T, L, with_text, lo, hi)
+    assert np.abs(o - ref).max() < 1e-12 and np.abs(lse - ref_lse).max() < 1e-12
+    of, lf = o64.attn_fwd_block_bh(q, k, v, T, L, True, 0, h * w)
+    o_all, l_all = o64.attn_fwd_bh(q, k, v, T, L)
+    assert np.array_equal(of, o_all) and np.array_equal(lf, l_all)
