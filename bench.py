@@ -7,6 +7,12 @@ already resident in HBM: the Q and K prologues (RMSNorm + gain + RoPE) and
 the attention forward; for a backward workload the step also runs the
 backward (attention + prologue gradients).  Prints ONE JSON line.
 
+By default every call is launched from the host each step; --graph captures
+each part of a step (prologues, forward call, backward call) once as a HIP
+graph and replays it (same kernels, arguments and buffers).  The default
+warmup is long on purpose: the GPU clock under MFMA load settles only after
+a few hundred calls, and a short warmup measures the ramp.
+
 value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
 with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).
 The attention-forward call (the V-to-FP16 tile pass and the attention kernel,
@@ -36,11 +42,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # defaults: ~0.1 s of untimed load first (the clock under MFMA load settles
+    # over the first few hundred calls), then ~0.1 s timed
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="1024sq")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each part of a step from a captured HIP graph instead of launching every call")
     ap.add_argument("--unfused-steps", type=int, default=10,
                     help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
     return ap.parse_args()
@@ -98,40 +108,62 @@ def main():
         ws = torch.empty(qi.bwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
         grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
 
-    ev = {n: [] for n in ("pro", "fwd", "bwd")}
-
-    def step(timed: bool):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
-        if timed:
-            e[0].record()
+    # the parts of a step, each a fixed sequence of library calls
+    def pro():
         qi.qknorm_rope(g["q"], g["g_q"], geo, out=qp)
         qi.qknorm_rope(g["k"], g["g_k"], geo, out=kp)
-        if timed:
-            e[1].record()
+
+    def fwd():
         qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of, workspace=fws)
-        if timed:
-            e[2].record()
-        if wl.backward:
-            qi.joint_attn_bwd(g["q"], g["k"], qp, kp, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo,
-                              workspace=ws, **grads)
-        if timed:
-            e[3].record()
-            ev["pro"].append((e[0], e[1]))
-            ev["fwd"].append((e[1], e[2]))
-            ev["bwd"].append((e[2], e[3]))
+
+    def bwd():
+        qi.joint_attn_bwd(g["q"], g["k"], qp, kp, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo,
+                          workspace=ws, **grads)
+
+    names = ["pro", "fwd"] + (["bwd"] if wl.backward else [])
+    parts = [pro, fwd] + ([bwd] if wl.backward else [])
+    for p in parts:  # eager once (device gate, first-launch costs)
+        p()
+    torch.cuda.synchronize()
+    if not args.graph:
+        runs = parts
+    else:
+        # Each part captured once as a HIP graph and replayed: the launches
+        # of a step reach the GPU without per-call host overhead, so no part
+        # waits for the host between kernels (the kernels, their arguments
+        # and buffers are the eager ones; the library allocates nothing).
+        graphs = []
+        for p in parts:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                p()
+            graphs.append(gr)
+        runs = [gr.replay for gr in graphs]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record()
+        for i, r in enumerate(runs):
+            r()
+            if e is not None:
+                e[i + 1].record()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
     def avg_ms(name):
-        return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
+        if name not in names:
+            return 0.0
+        j = names.index(name)
+        return float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
 
     pro_ms, fwd_ms, bwd_ms = avg_ms("pro"), avg_ms("fwd"), avg_ms("bwd")
     fwd_flops = wl.fwd_flops()
@@ -168,6 +200,7 @@ def main():
         "prologue_qk": {"ms": round(pro_ms, 4), "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
                         "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
+        "launch": "hip_graph_replay" if args.graph else "eager",
     }
     if wl.backward:
         bflops = wl.bwd_flops()
