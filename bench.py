@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true",
                     help="replay each part of a step from a captured HIP graph instead of launching every call")
+    ap.add_argument("--proj-steps", type=int, default=20,
+                    help="also time the QKV and output projections this many times (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=10,
                     help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
     return ap.parse_args()
@@ -207,6 +209,9 @@ def main():
         out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
                            "algorithmic_flops": bflops}
 
+    if args.proj_steps > 0:
+        out["projections"] = bench_proj(qi, torch, np, workloads, wl, args.proj_steps)
+
     if args.unfused_steps > 0:
         out["unfused_fwd"] = bench_unfused(qi, torch, np, wl, geo, qp, kp, g["v"], args.unfused_steps, fwd_ms)
 
@@ -215,6 +220,53 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, inp, qp, kp, o, lse, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_proj(qi, torch, np, workloads, wl, steps):
+    """The projections around the attention on the same shape (synthetic
+    per-stream weights): the packed QKV projection with the fused Q/K
+    prologue and the output projection, each timed with HIP events on the
+    launch stream against the dense BF16 MFMA peak (2 * tokens * N * D
+    FLOPs)."""
+    dev = "cuda:0"
+    geo = qi.Geometry(B=wl.B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w, txt_len=list(wl.txt_len),
+                      gain_streams=2)
+    p = {k: v.to(dev) for k, v in workloads.proj_inputs(wl, streams=2).items()}
+    D = wl.H * 128
+    x = p["x"].view(wl.B, wl.S, wl.H, 128)
+    o = p["o"].view(wl.B, wl.S, wl.H, 128)
+    q, k, v, y = (torch.empty_like(x) for _ in range(4))
+    ws = torch.empty(int(qi.lib().qi_qkv_proj_workspace(geo.ptr())), dtype=torch.uint8, device=dev)
+    tokens = wl.B * wl.S
+    flops = {"qkv_proj": 2.0 * tokens * 3 * D * D, "out_proj": 2.0 * tokens * D * D}
+    ev = {n: [] for n in flops}
+
+    def run(timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record()
+        qi.qkv_proj(x, p["w_qkv"], p["b_qkv"], geo, gain_q=p["g_q"], gain_k=p["g_k"], q=q, k=k, v=v, workspace=ws)
+        if timed:
+            e[1].record()
+        qi.attn_out_proj(o, p["w_o"], p["b_o"], geo, y=y)
+        if timed:
+            e[2].record()
+            ev["qkv_proj"].append((e[0], e[1]))
+            ev["out_proj"].append((e[1], e[2]))
+
+    for _ in range(max(5, steps // 4)):
+        run(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        run(True)
+    torch.cuda.synchronize()
+    res = {"steps": steps, "bound": "mfma", "peak_tflops": PEAK_BF16_TFLOPS, "weight_streams": 2,
+           "d_model": D, "tokens": tokens}
+    for n, f in flops.items():
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
+        tf = f / (ms * 1e-3) / 1e12
+        res[n] = {"ms": round(ms, 4), "flops": f, "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps, fused_ms):

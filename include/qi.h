@@ -265,6 +265,48 @@ int qi_joint_attn_av_gemm(const qi_geom* geom, const void* p, const float* alpha
                           const float* l, qi_bshd v, qi_bshd o, float* o_f32, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Projections around the attention ([Kernel list], rows qkv_bias_gemm and
+ * attn_out_bias_gemm; [Roadmap], "Model contract", row Streams: one weight
+ * set per stream).  D = H * 128 model channels; x, o and y are [B,S,H,128]
+ * views whose H * 128 channels of a token are contiguous (head stride 128).
+ * Weights are BF16 [weight_streams][N][D] (a linear layer's [out][in]
+ * layout), biases FP32 [weight_streams][N]; with weight_streams = 2, set 0
+ * serves the text tokens s < T_txt and set 1 the image tokens.
+ *   y[n] = bf16_rne( sum_k x[k] W[n][k] + bias[n] ),
+ * FP32 accumulation over k ascending (fixed order, no split-K), so a token's
+ * output bytes depend on its own row only.
+ */
+/* Bytes of workspace qi_qkv_proj needs with fuse_prologue = 1 (a table of
+ * the rotation's cos/sin per token position: S*64*2 FP32, rounded up to 256
+ * bytes); 0 for an invalid geometry. */
+size_t qi_qkv_proj_workspace(const qi_geom* geom);
+
+/*
+ * qi_qkv_proj -- packed Q/K/V projection, N = 3D output channels: channels
+ * 0..D-1 are Q (head h = channels 128h..128h+127), D..2D-1 K, 2D..3D-1 V.
+ * With fuse_prologue = 1 the Q and K outputs are the prologue of
+ * qi_qknorm_rope applied to the BF16 projections (gains gain_q, gain_k as
+ * there); the bytes equal qi_qkv_proj with fuse_prologue = 0 followed by
+ * qi_qknorm_rope on q and k, without their round trip through memory.
+ *   x        BF16 [B,S,H,128] hidden states.
+ *   q, k, v  BF16 [B,S,H,128] outputs.
+ *   workspace  with fuse_prologue = 1: at least qi_qkv_proj_workspace()
+ *            bytes, 256-byte aligned (scratch); else may be NULL.
+ */
+int qi_qkv_proj(const qi_geom* geom, qi_bshd x, const void* w, const float* bias,
+                int32_t weight_streams, const float* gain_q, const float* gain_k,
+                int32_t fuse_prologue, qi_bshd q, qi_bshd k, qi_bshd v, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qi_attn_out_proj -- output projection, N = D: y = o W^T + bias.
+ *   o        BF16 [B,S,H,128] attention output.
+ *   y        BF16 [B,S,H,128] output.
+ */
+int qi_attn_out_proj(const qi_geom* geom, qi_bshd o, const void* w, const float* bias,
+                     int32_t weight_streams, qi_bshd y, hipStream_t stream);
+
 /* Bytes of device workspace qi_joint_attn_bwd needs for this geometry. */
 size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
 

@@ -23,7 +23,8 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
 
 # every entry point declared in include/qi.h
 SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial",
-           "qi_joint_attn_merge", "qi_joint_attn_key_slots",
+           "qi_joint_attn_merge", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
+           "qi_joint_attn_key_slots",
            "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
            "qi_joint_attn_bwd", "qi_last_error", "qi_strict_probe", "qi_trace")
 
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_fwd_partial.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_merge.argtypes = [G, ctypes.c_int32, P, P, P, QiBshd, P, P, S]
+        L.qi_qkv_proj_workspace.argtypes = [G]
+        L.qi_qkv_proj_workspace.restype = ctypes.c_size_t
+        L.qi_qkv_proj.argtypes = [G, QiBshd, P, P, ctypes.c_int32, P, P, ctypes.c_int32, QiBshd, QiBshd, QiBshd, P,
+                                  ctypes.c_size_t, S]
+        L.qi_attn_out_proj.argtypes = [G, QiBshd, P, P, ctypes.c_int32, QiBshd, S]
         L.qi_joint_attn_key_slots.argtypes = [G]
         L.qi_joint_attn_key_slots.restype = ctypes.c_int64
         L.qi_joint_attn_qk_gemm.argtypes = [G, QiBshd, QiBshd, P, S]
@@ -80,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
         for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
+                     "qi_qkv_proj", "qi_attn_out_proj",
                      "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
                      "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_strict_probe"):
             getattr(L, name).restype = ctypes.c_int
@@ -191,6 +198,31 @@ def joint_attn_merge(acc, m, l, geom: Geometry, out=None, lse=None, out_f32=None
     _check(lib().qi_joint_attn_merge(geom.ptr(), int(n), _ptr(acc), _ptr(m), _ptr(l), _bshd(out), _ptr(lse),
                                      _ptr(out_f32), _stream()))
     return out, lse
+
+
+def qkv_proj(x, w, bias, geom: Geometry, gain_q=None, gain_k=None, fuse_prologue=True, q=None, k=None, v=None,
+             workspace=None):
+    """Per-stream packed QKV projection of x [B,S,H,128] (BF16) with weights
+    w [streams, 3D, D] (BF16) and bias [streams, 3D] (FP32).  With
+    fuse_prologue the Q and K outputs are already RMS-normalised, scaled by
+    the gains and rotated (the prologue).  Returns (q, k, v) BF16 [B,S,H,128]."""
+    q = torch.empty_like(x) if q is None else q
+    k = torch.empty_like(x) if k is None else k
+    v = torch.empty_like(x) if v is None else v
+    if fuse_prologue and workspace is None:
+        workspace = _empty((max(1, int(lib().qi_qkv_proj_workspace(geom.ptr()))),), torch.uint8, x)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qi_qkv_proj(geom.ptr(), _bshd(x), _ptr(w), _ptr(bias), int(w.shape[0]), _ptr(gain_q), _ptr(gain_k),
+                             int(bool(fuse_prologue)), _bshd(q), _bshd(k), _bshd(v), _ptr(workspace), nbytes,
+                             _stream()))
+    return q, k, v
+
+
+def attn_out_proj(o, w, bias, geom: Geometry, y=None):
+    """Per-stream output projection of o [B,S,H,128] (BF16): y = o W^T + b."""
+    y = torch.empty_like(o) if y is None else y
+    _check(lib().qi_attn_out_proj(geom.ptr(), _bshd(o), _ptr(w), _ptr(bias), int(w.shape[0]), _bshd(y), _stream()))
+    return y
 
 
 def key_slots(geom: Geometry) -> int:

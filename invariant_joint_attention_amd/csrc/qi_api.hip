@@ -245,6 +245,71 @@ void batch_txt_len(const qi_geom* g, int b0, int nb, int* dst) {
   for (int i = 0; i < kMaxBatchPerLaunch; ++i) dst[i] = i < nb ? g->txt_len[b0 + i] : 0;
 }
 
+// Projections: the input rows (a token's D = H*128 channels) must be
+// contiguous, and the loads address 64 rows from one base with 32-bit
+// offsets.
+int check_proj_common(const qi_geom* g, qi_bshd x, const void* w, const float* bias, int32_t weight_streams,
+                      int64_t N, std::vector<Extent>& ext) {
+  int rc;
+  if (weight_streams != 1 && weight_streams != 2)
+    return fail(QI_E_INVALID, "weight_streams=%d must be 1 or 2", weight_streams);
+  const int64_t D = (int64_t)g->H * kHeadDim;
+  if ((rc = check_view(g, x, 2, false, "x", ext))) return rc;
+  if (g->H > 1 && x.sh != kHeadDim)
+    return fail(QI_E_UNSUPPORTED, "x head stride %lld: a token's %lld channels must be contiguous",
+                (long long)x.sh, (long long)D);
+  if (seq_len(g) > 1 && x.ss > (int64_t(1) << 25))
+    return fail(QI_E_UNSUPPORTED, "x sequence stride above 2^25 elements");
+  if (D > (int64_t(1) << 24)) return fail(QI_E_UNSUPPORTED, "model width %lld too large", (long long)D);
+  if ((rc = check_dense(w, weight_streams * N * D * 2, false, "w", ext))) return rc;
+  if ((rc = check_dense(bias, weight_streams * N * 4, false, "bias", ext))) return rc;
+  return QI_OK;
+}
+
+int launch_proj(const qi_geom* g, qi_bshd x, const void* w, const float* bias, int weight_streams, int64_t N,
+                int sections, const qi_bshd* outs, int fuse, const float* gain_q, const float* gain_k,
+                float* rope, hipStream_t stream) {
+  int rc;
+  const int64_t S = seq_len(g);
+  if (fuse) {
+    RopeTableArgs t;
+    t.table = rope;
+    t.S = (int)S;
+    t.T_txt = g->T_txt;
+    t.gh = g->grid_h;
+    t.gw = g->grid_w;
+    t.theta = g->rope_theta;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)ceil_div(S * 64, 256)), dim3(256), 0, stream, t);
+    if ((rc = launched("rope_table_kernel"))) return rc;
+  }
+  ProjArgs a;
+  a.x = (const uint16_t*)x.data;
+  a.x_sb = x.sb;
+  a.x_ss = x.ss;
+  a.w = (const uint16_t*)w;
+  a.bias = bias;
+  a.weight_streams = weight_streams;
+  a.B = g->B;
+  a.S = (int)S;
+  a.T_txt = g->T_txt;
+  a.K = g->H * kHeadDim;
+  a.N = (int)N;
+  a.D = g->H * kHeadDim;
+  a.n_mt_txt = (int)ceil_div(g->T_txt, kProjTile);
+  a.n_mt_img = (int)ceil_div((int64_t)g->grid_h * g->grid_w, kProjTile);
+  a.n_nt = (int)ceil_div(N, kProjTile);
+  for (int i = 0; i < 3; ++i) a.out[i] = view_of<uint16_t>(outs[i < sections ? i : 0], 0);
+  a.fuse = fuse;
+  a.gain_q = gain_q;
+  a.gain_k = gain_k;
+  a.gain_streams = g->gain_streams;
+  a.eps = g->rms_eps;
+  a.rope = rope;
+  const int64_t grid = (int64_t)g->B * (a.n_mt_txt + a.n_mt_img) * a.n_nt;
+  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)grid), dim3(kProjWaves * 64), 0, stream, a);
+  return launched("proj_gemm_kernel");
+}
+
 BwdLayout bwd_layout(const qi_geom* g) {
   BwdLayout L;
   const int64_t S = seq_len(g);
@@ -500,6 +565,58 @@ int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc,
   return launched("attn_merge_kernel");
 }
 
+size_t qi_qkv_proj_workspace(const qi_geom* geom) {
+  if (check_geom(geom)) return 0;
+  return align256((size_t)seq_len(geom) * 64 * 2 * 4);
+}
+
+int qi_qkv_proj(const qi_geom* geom, qi_bshd x, const void* w, const float* bias, int32_t weight_streams,
+                const float* gain_q, const float* gain_k, int32_t fuse_prologue, qi_bshd q, qi_bshd k, qi_bshd v,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  if (fuse_prologue != 0 && fuse_prologue != 1)
+    return fail(QI_E_INVALID, "fuse_prologue=%d must be 0 or 1", fuse_prologue);
+  const int64_t D = (int64_t)geom->H * kHeadDim, N = 3 * D;
+  std::vector<Extent> ext;
+  if ((rc = check_proj_common(geom, x, w, bias, weight_streams, N, ext))) return rc;
+  const int64_t gbytes = (int64_t)geom->gain_streams * kHeadDim * 4;
+  if (fuse_prologue) {
+    if ((rc = check_dense(gain_q, gbytes, false, "gain_q", ext))) return rc;
+    if ((rc = check_dense(gain_k, gbytes, false, "gain_k", ext))) return rc;
+  }
+  if ((rc = check_view(geom, q, 2, true, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, true, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, true, "v", ext))) return rc;
+  const size_t ws_need = fuse_prologue ? qi_qkv_proj_workspace(geom) : 0;
+  if (fuse_prologue) {
+    if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+    if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+    if (workspace_bytes < ws_need)
+      return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
+    ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
+  }
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  const qi_bshd outs[3] = {q, k, v};
+  return launch_proj(geom, x, w, bias, weight_streams, N, 3, outs, fuse_prologue, gain_q, gain_k,
+                     (float*)workspace, stream);
+}
+
+int qi_attn_out_proj(const qi_geom* geom, qi_bshd o, const void* w, const float* bias, int32_t weight_streams,
+                     qi_bshd y, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  const int64_t D = (int64_t)geom->H * kHeadDim;
+  std::vector<Extent> ext;
+  if ((rc = check_proj_common(geom, o, w, bias, weight_streams, D, ext))) return rc;
+  if ((rc = check_view(geom, y, 2, true, "y", ext))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  const qi_bshd outs[3] = {y, y, y};
+  return launch_proj(geom, o, w, bias, weight_streams, D, 1, outs, 0, nullptr, nullptr, nullptr, stream);
+}
+
 int64_t qi_joint_attn_key_slots(const qi_geom* geom) {
   if (check_geom(geom)) return 0;
   return (int64_t)fwd_nt_max(geom) * kFwdBN;
@@ -729,7 +846,10 @@ const char* qi_trace(void) {
     snprintf(buf, sizeof buf,
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\",\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\",\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\","
+             "\"qkv_proj\":\"proj_gemm_kernel\",\"out_proj\":\"proj_gemm_kernel\",\"rope_table\":\"rope_table_kernel\","
+             "\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
              "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","

@@ -153,6 +153,34 @@ __global__ void attn_qk_kernel(QkArgs a);
 __global__ void attn_softmax_kernel(SoftmaxArgs a);
 __global__ void attn_av_kernel(AvArgs a);
 
+// Projections around the attention (per-stream weights, Y = X W^T + bias).
+constexpr int kProjTile = 256;  // tokens and channels per workgroup tile
+constexpr int kProjTK = 64;     // K-elements per LDS stage
+constexpr int kProjWaves = 8;
+struct ProjArgs {
+  const uint16_t* x;  // BF16 rows of K elements: token s of sample b at x + b*x_sb + s*x_ss
+  int64_t x_sb, x_ss;
+  const uint16_t* w;  // BF16 [weight_streams][N][K]
+  const float* bias;  // FP32 [weight_streams][N]
+  int weight_streams;
+  int B, S, T_txt, K, N, D;  // N = sections * D output channels
+  int n_mt_txt, n_mt_img, n_nt;
+  View<uint16_t> out[3];  // section i (channels i*D .. i*D + D - 1) as [B,S,H,128]
+  int fuse;               // 1: sections 0 and 1 (Q, K) go through the RMSNorm + gain + RoPE prologue
+  const float* gain_q;
+  const float* gain_k;  // FP32 [gain_streams][128]
+  int gain_streams;
+  float eps;
+  const float* rope;  // FP32 [S][64][2]: (cos, sin) per token position and pair
+};
+struct RopeTableArgs {
+  float* table;  // [S][64][2]
+  int S, T_txt, gh, gw;
+  double theta;
+};
+__global__ void proj_gemm_kernel(ProjArgs a);
+__global__ void rope_table_kernel(RopeTableArgs a);
+
 __global__ void attn_bwd_dq_kernel(BwdArgs a);
 __global__ void attn_bwd_dk_kernel(BwdArgs a);
 __global__ void attn_bwd_dv_kernel(BwdArgs a);

@@ -561,3 +561,30 @@ void oracle_qknorm_rope_bwd(int B, int S, int H, int T_txt, int gh, int gw,
   free(U);
   free(pos);
 }
+
+/* -------------------------------------------------------------------------
+ * Projections around the attention  [Kernel list, rows qkv_bias_gemm (the
+ * packed Q/K/V projection, 3072 -> 3 x 3072 plus bias, one weight set per
+ * stream) and attn_out_bias_gemm (the output projection 3072 -> 3072 plus
+ * bias, per stream); Roadmap, "Model contract", row Streams: text and image
+ * tokens keep separate weights].
+ *
+ * y[i][n] = sum_k x[i][k] W[n][k] + bias[n] for rows i of x [n_rows][K] and
+ * W [N][K] (the layout of a linear layer's weight), the sum in ascending k.
+ * ---------------------------------------------------------------------- */
+void oracle_linear(int64_t n_rows, int K, int N, const real* x, const real* W,
+                   const real* bias, real* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const real* xi = x + i * K;
+    for (int n = 0; n < N; ++n) {
+      const real* wn = W + (int64_t)n * K;
+      real acc = 0;
+      for (int k = 0; k < K; ++k) {
+        real pr = xi[k] * wn[k];
+        acc = acc + pr;
+      }
+      y[i * N + n] = acc + bias[n];
+    }
+  }
+}

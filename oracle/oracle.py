@@ -238,6 +238,32 @@ class Oracle:
         return tuple(outs)
 
 
+    # ----------------------------------------------------------- projections
+    def linear(self, x, W, bias):
+        """y = x W^T + bias for x [n, K], W [N, K], bias [N]; the sum over k
+        ascending."""
+        x, W, bias = self._r(x), self._r(W), self._r(bias)
+        n, K = x.shape
+        N = W.shape[0]
+        assert W.shape == (N, K) and bias.shape == (N,)
+        y = np.empty((n, N), dtype=self.dtype)
+        self.lib.oracle_linear(ctypes.c_int64(n), ctypes.c_int(K), ctypes.c_int(N), _ptr(x, self.creal),
+                               _ptr(W, self.creal), _ptr(bias, self.creal), _ptr(y, self.creal))
+        return y
+
+    def stream_linear(self, x, W, bias, T_txt):
+        """Per-stream projection of x [B, S, K]: text rows s < T_txt use
+        W[0], bias[0]; image rows use the last set (one set: shared)."""
+        B, S, K = x.shape
+        W, bias = np.asarray(W), np.asarray(bias)
+        out = np.empty((B, S, W.shape[1]), dtype=self.dtype)
+        for b in range(B):
+            if T_txt:
+                out[b, :T_txt] = self.linear(x[b, :T_txt], W[0], bias[0])
+            out[b, T_txt:] = self.linear(x[b, T_txt:], W[-1], bias[-1])
+        return out
+
+
 def fold_batch(per_sample: np.ndarray) -> np.ndarray:
     """Sum per-sample partials over the batch in ascending order."""
     acc = np.zeros(per_sample.shape[1:], dtype=per_sample.dtype)
@@ -273,3 +299,20 @@ def backward_path(orc: Oracle, x_q, x_k, v, g_q, g_k, dO, txt_len, T_txt, h, w):
     dk, dgk = orc.qknorm_rope_bwd(orc.widen(x_k), g_k, dkp, T_txt, h, w)
     return dict(fw=fw, dq_pre=dqp, dk_pre=dkp, dv=dv, dq=dq, dk=dk,
                 dgq_ps=dgq, dgk_ps=dgk, dgq=fold_batch(dgq), dgk=fold_batch(dgk))
+
+
+def qkv_path(orc: Oracle, x, W, bias, g_q, g_k, T_txt, h, w):
+    """The packed QKV projection and the Q/K prologue from BF16 bit patterns.
+
+    x: uint16 [B, S, D] hidden states (D = H*128); W: uint16 [streams, 3D, D];
+    bias: float [streams, 3D].  The projection output is rounded once to BF16
+    (its declared output), then Q and K go through the prologue.  Returns the
+    BF16 bit patterns of q', k', v and the projections q, k."""
+    B, S, D = x.shape
+    H = D // HD
+    y = orc.stream_linear(orc.widen(x), orc.widen(W), bias, T_txt)
+    yb = orc.cast_bf16(y)
+    q, k, v = (yb[..., i * D:(i + 1) * D].reshape(B, S, H, HD) for i in range(3))
+    qp = orc.cast_bf16(orc.qknorm_rope(orc.widen(q), g_q, T_txt, h, w))
+    kp = orc.cast_bf16(orc.qknorm_rope(orc.widen(k), g_k, T_txt, h, w))
+    return dict(q=q, k=k, v=v, q_prime=qp, k_prime=kp, y=y)

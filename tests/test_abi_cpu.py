@@ -297,3 +297,44 @@ def test_block_forward_and_merge_validation():
     assert merge(lse=region(5)) == code("QI_E_ALIAS")
     assert merge(o=fake_bshd(region(4), g.B, g.S, g.H)) == code("QI_E_ALIAS")
     assert merge(of=region(6) + 16) == code("QI_E_ALIAS")
+
+
+def test_projection_validation():
+    """QKV and output projections: weights, streams, contiguity of a token's
+    channels, outputs and workspace are checked before any launch."""
+    g = geom()  # H = 2: D = 256
+    L = qi.lib()
+    D = 256
+    x = fake_bshd(region(0), g.B, g.S, g.H)
+    outs = [fake_bshd(region(3 + i), g.B, g.S, g.H) for i in range(3)]
+    ws = L.qi_qkv_proj_workspace(g.ptr())
+    assert ws == -(-(g.S * 64 * 2 * 4) // 256) * 256
+
+    def qkv(x=x, w=region(1), bias=region(2), streams=2, gq=region(7), gk=region(8), fuse=1, outs=outs,
+            ws_ptr=region(9), ws_bytes=ws):
+        return L.qi_qkv_proj(g.ptr(), x, w, bias, streams, gq, gk, fuse, *outs, ws_ptr, ws_bytes, None)
+
+    assert qkv() == code("QI_E_UNSUPPORTED")  # valid: stops at the device gate
+    assert qkv(fuse=0, gq=None, gk=None, ws_ptr=None, ws_bytes=0) == code("QI_E_UNSUPPORTED")
+    assert qkv(streams=3) == code("QI_E_INVALID")
+    assert qkv(fuse=2) == code("QI_E_INVALID")
+    assert qkv(w=None) == code("QI_E_INVALID")
+    assert qkv(gq=None) == code("QI_E_INVALID")
+    assert qkv(ws_ptr=None) == code("QI_E_WORKSPACE")
+    assert qkv(ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    assert qkv(bias=region(2) + 4) == code("QI_E_ALIGN")
+    # a token's channels must be contiguous (head stride 128)
+    assert qkv(x=fake_bshd(region(0), g.B, g.S, g.H, sh=256, ss=512)) == code("QI_E_UNSUPPORTED")
+    # outputs may not overlap the weights or each other
+    assert qkv(outs=[fake_bshd(region(1), g.B, g.S, g.H)] + outs[1:]) == code("QI_E_ALIAS")
+    assert qkv(outs=[outs[0], outs[0], outs[2]]) == code("QI_E_ALIAS")
+    # the weight array spans streams * 3D * D BF16 values: an output right after its start overlaps
+    assert qkv(outs=[fake_bshd(region(1) + 2 * 3 * D * D, g.B, g.S, g.H)] + outs[1:]) == code("QI_E_ALIAS")
+
+    def out(o=x, w=region(1), bias=region(2), streams=1, y=outs[0]):
+        return L.qi_attn_out_proj(g.ptr(), o, w, bias, streams, y, None)
+
+    assert out() == code("QI_E_UNSUPPORTED")
+    assert out(streams=0) == code("QI_E_INVALID")
+    assert out(y=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    assert out(bias=None) == code("QI_E_INVALID")

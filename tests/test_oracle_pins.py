@@ -614,3 +614,30 @@ def test_block_attention_matches_sdpa(o64, case):
     of, lf = o64.attn_fwd_block_bh(q, k, v, T, L, True, 0, h * w)
     o_all, l_all = o64.attn_fwd_bh(q, k, v, T, L)
     assert np.array_equal(of, o_all) and np.array_equal(lf, l_all)
+
+
+# ------------------------------------------------------------ projections
+def test_linear_matches_numpy(o64):
+    """y = x W^T + b against numpy's float64 matmul, on shapes with odd K, N."""
+    rng = _rng(21)
+    for n, K, N in ((1, 1, 1), (7, 130, 33), (64, 256, 384)):
+        x, W, b = rng.standard_normal((n, K)), rng.standard_normal((N, K)), rng.standard_normal(N)
+        y = o64.linear(x, W, b)
+        assert np.abs(y - (x @ W.T + b)).max() <= 1e-12 * max(1.0, np.abs(x @ W.T).max())
+
+
+def test_stream_linear_selects_weights_by_segment(o64):
+    """Text rows use weight set 0, image rows the last set: with W_img = 0 the
+    image rows equal the image bias exactly, and with one set both agree."""
+    rng = _rng(22)
+    B, T, S, K, N = 2, 5, 12, 16, 8
+    x = rng.standard_normal((B, S, K))
+    W = np.stack([rng.standard_normal((N, K)), np.zeros((N, K))])
+    b = rng.standard_normal((2, N))
+    y = o64.stream_linear(x, W, b, T)
+    assert np.array_equal(y[:, T:], np.broadcast_to(b[1], (B, S - T, N)))
+    assert np.abs(y[:, :T] - (x[:, :T] @ W[0].T + b[0])).max() < 1e-12
+    y1 = o64.stream_linear(x, W[:1], b[:1], T)
+    assert np.abs(y1 - (x @ W[0].T + b[0])).max() < 1e-12
+    y0 = o64.stream_linear(x, W, b, 0)  # no text rows
+    assert np.array_equal(y0, np.broadcast_to(b[1], (B, S, N)))

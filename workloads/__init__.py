@@ -130,3 +130,28 @@ def av_operands(B: int, H: int, S: int, key_slots: int, seed: int) -> dict:
     alpha = 0.25 + 0.75 * torch.rand(B, H, S, key_slots // 64, generator=g)
     l = 1 + 63 * torch.rand(B, H, S, generator=g)
     return dict(p=p, alpha=alpha, l=l)
+
+
+def proj_inputs(wl: Workload, streams: int = 2, seed_offset: int = 1000) -> dict:
+    """Inputs of the projections around the attention (the model's packed QKV
+    projection and output projection, D = H*128 channels), drawn on the CPU:
+    hidden states x ~ N(0,1) and attention output o ~ N(0,1) in BF16
+    [B, S, D]; per-stream weights W_qkv [streams, 3D, D] and W_o [streams, D,
+    D] ~ N(0, 1/D) in BF16 (outputs of unit scale), biases b_qkv [streams, 3D]
+    and b_o [streams, D] ~ N(0, 0.02^2) in FP32; RMSNorm gains g_q, g_k
+    [streams, 128] ~ 1 + 0.1 N(0,1).  Draw order as listed."""
+    g = torch.Generator("cpu").manual_seed(wl.seed + seed_offset)
+    B, S, D = wl.B, wl.S, wl.H * HEAD_DIM
+
+    def bf16(*shape, std=1.0):
+        return (std * torch.randn(*shape, generator=g, dtype=torch.float32)).to(torch.bfloat16)
+
+    x = bf16(B, S, D)
+    o = bf16(B, S, D)
+    w_qkv = bf16(streams, 3 * D, D, std=D ** -0.5)
+    w_o = bf16(streams, D, D, std=D ** -0.5)
+    b_qkv = 0.02 * torch.randn(streams, 3 * D, generator=g, dtype=torch.float32)
+    b_o = 0.02 * torch.randn(streams, D, generator=g, dtype=torch.float32)
+    gq = 1.0 + 0.1 * torch.randn(streams, HEAD_DIM, generator=g, dtype=torch.float32)
+    gk = 1.0 + 0.1 * torch.randn(streams, HEAD_DIM, generator=g, dtype=torch.float32)
+    return dict(x=x, o=o, w_qkv=w_qkv, w_o=w_o, b_qkv=b_qkv, b_o=b_o, g_q=gq, g_k=gk)
