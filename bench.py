@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true",
                     help="replay each part of a step from a captured HIP graph instead of launching every call")
-    ap.add_argument("--proj-steps", type=int, default=20,
+    ap.add_argument("--proj-steps", type=int, default=50,
                     help="also time the QKV and output projections this many times (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=10,
                     help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
@@ -254,7 +254,7 @@ def bench_proj(qi, torch, np, workloads, wl, steps):
             ev["qkv_proj"].append((e[0], e[1]))
             ev["out_proj"].append((e[1], e[2]))
 
-    for _ in range(max(5, steps // 4)):
+    for _ in range(steps):
         run(False)
     torch.cuda.synchronize()
     for _ in range(steps):
