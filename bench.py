@@ -280,7 +280,7 @@ def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps, fused_ms):
     nt = Kp // 64
     s = torch.empty((B, H, S, Kp), dtype=torch.float32, device=dev)
     p = torch.empty((B, H, S, Kp), dtype=torch.float16, device=dev)
-    alpha = torch.empty((B, H, S, nt), dtype=torch.float32, device=dev)
+    alpha = torch.empty((B, H, nt, S), dtype=torch.float32, device=dev)
     l = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)

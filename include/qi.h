@@ -210,8 +210,9 @@ int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc,
  * reproduce the unfused result byte for byte).  They hold the same per-row
  * arithmetic as the fused kernel with the intermediates in HBM.
  *
- * Intermediates are dense FP32 / FP16 arrays indexed [b][h][i][slot] for
- * query row i, with Kp = qi_joint_attn_key_slots() slots per row:
+ * Scores and P are dense arrays indexed [b][h][i][slot] for query row i
+ * (alpha is tile-major: [b][h][t][i]), with Kp = qi_joint_attn_key_slots()
+ * slots per row:
  * Kp = 64 * nt with nt = ceil(T_txt/64) + ceil(grid_h*grid_w/64) logical key
  * tiles; slot 64*t + j is key j of tile t of row b, where row b's tiles are
  * ceil(txt_len[b]/64) text tiles (keys 64t ...) followed by the image tiles
@@ -243,7 +244,8 @@ int qi_joint_attn_qk_gemm(const qi_geom* geom, qi_bshd q, qi_bshd k, float* scor
  *   scores   FP32 dense [B][H][S][Kp] from qi_joint_attn_qk_gemm.
  *   p        FP16 dense [B][H][S][Kp] output: p rounded to nearest even;
  *            masked slots 0.
- *   alpha    FP32 dense [B][H][S][Kp/64] output (1 for unused tiles).
+ *   alpha    FP32 dense [B][H][Kp/64][S] output, tile-major (1 for unused
+ *            tiles).
  *   l        FP32 dense [B][H][S] output: the row sum of the FP32 p.
  *   lse      FP32 dense [B][H][S] output.
  */

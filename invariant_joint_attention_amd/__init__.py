@@ -240,11 +240,11 @@ def joint_attn_qk_gemm(q, k, geom: Geometry, scores=None):
 
 def joint_attn_softmax(scores, geom: Geometry, p=None, alpha=None, l=None, lse=None):
     """Online softmax over the key tiles of FP32 scores [B, H, S, key_slots].
-    Returns (P FP16 [B,H,S,slots], alpha FP32 [B,H,S,slots/64], l FP32
-    [B,H,S], LSE FP32 [B,H,S])."""
+    Returns (P FP16 [B,H,S,slots], alpha FP32 [B,H,slots/64,S] (tile-major),
+    l FP32 [B,H,S], LSE FP32 [B,H,S])."""
     B, H, S, Kp = geom.B, geom.H, geom.S, key_slots(geom)
     p = _empty((B, H, S, Kp), torch.float16, scores) if p is None else p
-    alpha = _empty((B, H, S, Kp // 64), torch.float32, scores) if alpha is None else alpha
+    alpha = _empty((B, H, Kp // 64, S), torch.float32, scores) if alpha is None else alpha
     l = _empty((B, H, S), torch.float32, scores) if l is None else l
     lse = _empty((B, H, S), torch.float32, scores) if lse is None else lse
     _check(lib().qi_joint_attn_softmax(geom.ptr(), _ptr(scores), _ptr(p), _ptr(alpha), _ptr(l), _ptr(lse), _stream()))

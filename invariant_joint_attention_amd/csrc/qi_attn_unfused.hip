@@ -91,8 +91,12 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t off32, uint32_t 
 
 }  // namespace
 
+// Score staging per wave: 32 rows x 256 bytes, chunk c of row r at chunk
+// c ^ (r & 15), so each store writes whole 256-byte row pieces.
+constexpr int kQkStageB = 32 * 256;
+
 __global__ __launch_bounds__(kQkWaves * 64) void attn_qk_kernel(QkArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileB + kQkWaves * kQkStageB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, hh = lane >> 5;
@@ -108,7 +112,9 @@ __global__ __launch_bounds__(kQkWaves * 64) void attn_qk_kernel(QkArgs a) {
     if (qrow < a.S) z = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
     q[kk] = __builtin_bit_cast(bf16x8, z);
   }
-  float* const srow = a.s + (((int64_t)b * a.H + h) * a.S + qrow) * Kp;
+  const int row0 = blockIdx.x * (kQkWaves * 32) + wave * 32;  // the wave's first row
+  float* const srow0 = a.s + (((int64_t)b * a.H + h) * a.S + row0) * Kp;
+  char* const stage = smem + 2 * kTileB + wave * kQkStageB;
 
   // Waves 0-3 fill the K tiles, 16 rows each; rows past a tile's valid count
   // are zero in LDS (their scores are masked).
@@ -156,16 +162,22 @@ __global__ __launch_bounds__(kQkWaves * 64) void attn_qk_kernel(QkArgs a) {
         if (wave < 4 && t + 2 < rt.nt) load(t + 2);
       }
     }
-    if (qrow < a.S) {
+    // this lane's keys 32kb + 8g + 4hh .. +3 of row lr are chunk 8kb + 2g + hh
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = score_key(kb, 4 * g + e, hh) < nv ? s[kb][4 * g + e] : -INFINITY;
-          *(f32x4*)(srow + kFwdBN * t + 32 * kb + 8 * g + 4 * hh) = v;
-        }
+        for (int e = 0; e < 4; ++e) v[e] = score_key(kb, 4 * g + e, hh) < nv ? s[kb][4 * g + e] : -INFINITY;
+        *(f32x4*)(stage + lr * 256 + 16 * ((8 * kb + 2 * g + hh) ^ (lr & 15))) = v;
+      }
+    // store i, lane l: row 4i + l/16, chunk l%16 (the rows' 256 bytes of tile t)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const f32x4 v = *(const f32x4*)(stage + r * 256 + 16 * (c ^ (r & 15)));
+      if (row0 + r < a.S) *(f32x4*)(srow0 + (int64_t)r * Kp + kFwdBN * t + 4 * c) = v;
     }
   }
 }
@@ -210,7 +222,7 @@ __global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(Softma
   // this lane's logical chunk 8kb + 2g + hh of row lr sits at chunk (8kb + 2g) ^ (hh ^ swz(lr))
   const uint32_t frag0 = addr_of(wbuf) + (uint32_t)(lr * 256 + 16 * (hh ^ swz(lr)));
   uint16_t* const prow0 = a.p + (bh * a.S + row0) * Kp;
-  float* const arow = a.alpha + (bh * a.S + min(qrow, a.S - 1)) * a.nt_max;
+  float* const acol = a.alpha + bh * a.nt_max * a.S + qrow;  // alpha of tile t at acol[t * S]
 
   float m_used = -INFINITY, l = 0.f;
   load_scores(0);
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(Softma
         *(u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * c) = po[i];
       }
     }
-    if (store && hh == 0) arow[t] = alpha;
+    if (store && hh == 0) acol[(int64_t)t * a.S] = alpha;
   }
   // tiles past this row's count: P = 0, alpha = 1
   for (int t = rt.nt; t < a.nt_max; ++t) {
@@ -286,7 +298,7 @@ __global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(Softma
       const int r = 8 * i + (lane >> 3);
       if (row0 + r < a.S) *(u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * (lane & 7)) = z;
     }
-    if (store && hh == 0) arow[t] = 1.0f;
+    if (store && hh == 0) acol[(int64_t)t * a.S] = 1.0f;
   }
   const uint32_t lu = __float_as_uint(l);
   const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
@@ -328,15 +340,15 @@ __global__ __launch_bounds__(kAvWaves * 64) void attn_av_kernel(AvArgs a) {
     const int rr = min(row0 + r, a.S - 1) - base_row;
     poff[i] = (uint32_t)rr * (uint32_t)(Kp * 2) + 16u * (uint32_t)((lane & 7) ^ (r & 7));
   }
-  // alpha of this lane's row: scalar base at the wave's first row
-  const char* const abase = (const char*)(a.alpha + (bh * a.S + base_row) * a.nt_max);
-  const uint32_t aoff = (uint32_t)(min(qrow, a.S - 1) - base_row) * (uint32_t)(a.nt_max * 4);
+  // alpha of this lane's row in tile t: scalar base at the wave's first row of tile t
+  const char* const abase = (const char*)(a.alpha + bh * a.nt_max * a.S + base_row);
+  const uint32_t aoff = (uint32_t)(min(qrow, a.S - 1) - base_row) * 4u;
   auto load_p = [&](int t) {
     const char* src = pbase + (int64_t)t * kFwdBN * 2;
     const uint32_t dst = addr_of(pbuf);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(src, poff[i], dst + 1024u * i);
-    dma4(abase, aoff + 4u * (uint32_t)t, addr_of(abuf));
+    dma4(abase + (int64_t)t * a.S * 4, aoff, addr_of(abuf));
   };
   const uint16_t* const vt_bh = a.vt + bh * a.nt_max * kVtileElems;
   const VtOff vo = vt_offsets(lane);

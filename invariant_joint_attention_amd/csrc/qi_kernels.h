@@ -133,7 +133,7 @@ struct QkArgs {
 struct SoftmaxArgs {
   const float* s;  // [B][H][S][Kp]
   uint16_t* p;     // FP16 P [B][H][S][Kp]; masked = 0
-  float* alpha;    // FP32 rescale factor of tile t [B][H][S][nt_max]; unused tiles = 1
+  float* alpha;    // FP32 rescale factor of tile t [B][H][nt_max][S] (tile-major); unused tiles = 1
   float* l;        // FP32 row sum [B][H][S]
   float* lse;      // FP32 [B][H][S]
   int S, H, T_txt, T_img, nt_max;

@@ -113,9 +113,10 @@ def test_composition_equals_fused_small(spec):
         assert torch.isfinite(s[b][..., ~masked]).all()
         assert (p[b][..., masked] == 0).all()
         n_b = len(_tiles(wl.T_txt, wl.txt_len[b], wl.S))
-        assert (alpha[b][..., n_b:] == 1).all()
-        assert (alpha[b][..., 0] == 0).all()  # nothing accumulated before the first tile
-        assert ((alpha[b][..., :n_b] >= 0) & (alpha[b][..., :n_b] <= 1)).all()
+        ab = alpha[b]  # [H, tiles, S]
+        assert (ab[:, n_b:] == 1).all()
+        assert (ab[:, 0] == 0).all()  # nothing accumulated before the first tile
+        assert ((ab[:, :n_b] >= 0) & (ab[:, :n_b] <= 1)).all()
 
 
 @pytest.mark.parametrize("cfg", ["1024sq", "1328sq_cfg", "1664x928"])
@@ -203,7 +204,7 @@ def test_softmax_against_oracle(o64, spec):
             s_keys = np.zeros((wl.S, wl.S))
             s_keys[:, key[live]] = raw[b, h].double().numpy()[:, live] * sc
             p_ref, lse_ref = o64.attn_softmax_rows(s_keys, wl.T_txt, L)
-            a = alpha[b, h]
+            a = alpha[b, h].T  # [S, tiles]
             # weight of tile t in the final sum: product of the later tiles' factors
             later = np.ones((wl.S, Kp // 64))
             for t in range(nt - 2, -1, -1):
@@ -248,7 +249,7 @@ def test_av_gemm_against_oracle(o64, spec):
         n_adds = 16 + 4 * nt_b
         for h in range(wl.H):
             P = f64(ops["p"][b, h]).reshape(wl.S, Kp // 64, 64)
-            al, lv = f64(ops["alpha"][b, h]), f64(ops["l"][b, h])
+            al, lv = f64(ops["alpha"][b, h]).T.copy(), f64(ops["l"][b, h])
             vb = f64(v[b, :, h])
             ref = o64.attn_av_rows(P, al, lv, vb, wl.T_txt, L)
             mag = o64.attn_av_rows(P, al, lv, np.abs(vb), wl.T_txt, L)

@@ -123,11 +123,11 @@ def score_operands(B: int, H: int, S: int, key_slots: int, seed: int) -> torch.T
 
 def av_operands(B: int, H: int, S: int, key_slots: int, seed: int) -> dict:
     """Operands of the A.V operator on its own: P FP16 uniform in [0, 2)
-    [B, H, S, key_slots], alpha FP32 uniform in [1/4, 1] [B, H, S, key_slots/64],
-    l FP32 uniform in [1, 64) [B, H, S]."""
+    [B, H, S, key_slots], alpha FP32 uniform in [1/4, 1] [B, H, key_slots/64, S]
+    (tile-major), l FP32 uniform in [1, 64) [B, H, S]."""
     g = torch.Generator("cpu").manual_seed(seed)
     p = (2 * torch.rand(B, H, S, key_slots, generator=g)).to(torch.float16)
-    alpha = 0.25 + 0.75 * torch.rand(B, H, S, key_slots // 64, generator=g)
+    alpha = 0.25 + 0.75 * torch.rand(B, H, key_slots // 64, S, generator=g)
     l = 1 + 63 * torch.rand(B, H, S, generator=g)
     return dict(p=p, alpha=alpha, l=l)
 
