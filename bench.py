@@ -53,6 +53,8 @@ def parse():
                     help="replay each part of a step from a captured HIP graph instead of launching every call")
     ap.add_argument("--proj-steps", type=int, default=50,
                     help="also time the QKV and output projections this many times (0: skip)")
+    ap.add_argument("--block-steps", type=int, default=20,
+                    help="also time the key-block forward (image keys in blocks of 512) and the merge (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=10,
                     help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
     return ap.parse_args()
@@ -209,6 +211,9 @@ def main():
         out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
                            "algorithmic_flops": bflops}
 
+    if args.block_steps > 0:
+        out["blocks"] = bench_blocks(qi, torch, np, wl, geo, qp, kp, g["v"], args.block_steps, fwd_ms)
+
     if args.proj_steps > 0:
         out["projections"] = bench_proj(qi, torch, np, workloads, wl, args.proj_steps)
 
@@ -220,6 +225,59 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, inp, qp, kp, o, lse, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, fused_ms, block=512):
+    """The key-block forward as a sequence-parallel split would run it: the
+    image keys in blocks of `block` keys (the text keys in block 0), one
+    partial call per block, then the fixed-order merge; each timed with HIP
+    events on the launch stream.  The partial calls together perform the
+    whole forward's algorithmic FLOPs; the merge is HBM-bound (it reads n row
+    states of 520 bytes and writes O)."""
+    dev = q.device
+    B, H, S, T_img = wl.B, wl.H, wl.S, wl.T_img
+    edges = list(range(0, T_img, block)) + [T_img]
+    blocks = [(i == 0, edges[i], edges[i + 1]) for i in range(len(edges) - 1)]
+    n = len(blocks)
+    acc = torch.empty((n, B, H, S, 128), dtype=torch.float32, device=dev)
+    m = torch.empty((n, B, H, S), dtype=torch.float32, device=dev)
+    l = torch.empty((n, B, H, S), dtype=torch.float32, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    ws = torch.empty(qi.fwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
+    ev = {"partials": [], "merge": []}
+
+    def run(timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record()
+        for i, (wt, lo, hi) in enumerate(blocks):
+            qi.joint_attn_fwd_partial(q, k, v, geo, wt, lo, hi, acc=acc[i], m=m[i], l=l[i], workspace=ws)
+        if timed:
+            e[1].record()
+        qi.joint_attn_merge(acc, m, l, geo, out=o, lse=lse)
+        if timed:
+            e[2].record()
+            ev["partials"].append((e[0], e[1]))
+            ev["merge"].append((e[1], e[2]))
+
+    for _ in range(steps):
+        run(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        run(True)
+    torch.cuda.synchronize()
+    p_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["partials"]]))
+    m_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["merge"]]))
+    flops = wl.fwd_flops()
+    rows = B * H * S
+    m_bytes = n * rows * (128 * 4 + 8) + rows * 128 * 2 + rows * 4
+    return {"steps": steps, "block_keys": block, "n_blocks": n,
+            "partials": {"ms": round(p_ms, 4), "tflops": round(flops / (p_ms * 1e-3) / 1e12, 1),
+                         "frac": round(flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"},
+            "merge": {"ms": round(m_ms, 4), "bytes": m_bytes, "gbps": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
+                      "frac": round(m_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bound": "hbm"},
+            "ms": round(p_ms + m_ms, 4), "vs_fused": round((p_ms + m_ms) / fused_ms, 3)}
 
 
 def bench_proj(qi, torch, np, workloads, wl, steps):

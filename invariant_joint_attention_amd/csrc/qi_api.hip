@@ -367,6 +367,9 @@ int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_
     c.T_img = a.T_img;
     c.nt_max = nt_max;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
+    c.with_text = a.blk_text;
+    c.img_t0 = blk ? a.blk_img_t0 : 0;
+    c.img_t1 = blk ? a.blk_img_t1 : nt_max;
     hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
                        c);
     if ((rc = launched("v_tiles_kernel"))) return rc;
@@ -739,6 +742,9 @@ int qi_joint_attn_av_gemm(const qi_geom* geom, const void* p, const float* alpha
     c.T_img = a.T_img;
     c.nt_max = (int)nt_max;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) c.txt_len[i] = a.txt_len[i];
+    c.with_text = 1;
+    c.img_t0 = 0;
+    c.img_t1 = (int)nt_max;
     hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
                        c);
     if ((rc = launched("v_tiles_kernel"))) return rc;

@@ -483,7 +483,8 @@ __global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_partial_kernel(Fwd
 // conversion rounds to nearest even), the keys of each 16-key chunk in the
 // A.V reduction order (position p holds key p with bits 2 and 3 swapped).
 // Keys past the tile's valid count are written as zero, so the attention
-// kernel loads whole tiles and a masked key's V slot is exactly zero.
+// kernel loads whole tiles and a masked key's V slot is exactly zero.  For a
+// key-block forward only the block's tiles are converted.
 __global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {
   __shared__ uint32_t tl[kFwdBN][kHeadDim / 2 + 1];  // [key][channel pair]; one pad word per row
   const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -491,6 +492,7 @@ __global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {
   const int ntxt = (L + kFwdBN - 1) / kFwdBN;
   const int nt = ntxt + (a.T_img + kFwdBN - 1) / kFwdBN;
   if (t >= nt) return;
+  if (t < ntxt ? !a.with_text : (t - ntxt < a.img_t0 || t - ntxt >= a.img_t1)) return;  // outside the key block
   int key0, nvalid;
   tile_bounds(t, ntxt, L, a.T_txt, a.T_img, key0, nvalid);
   for (int i = threadIdx.x; i < kFwdBN * 16; i += 256) {

@@ -113,6 +113,8 @@ struct VtileArgs {
   uint16_t* out;           // FP16 [B][H][nt_max][128][64]
   int H, T_txt, T_img, nt_max;
   int txt_len[kMaxBatchPerLaunch];
+  // tiles converted: the text tiles when with_text, image tiles img_t0 <= t' < img_t1
+  int with_text, img_t0, img_t1;
 };
 __global__ void v_tiles_kernel(VtileArgs a);
 
