@@ -14,7 +14,9 @@ warmup is long on purpose: the GPU clock under MFMA load settles only after
 a few hundred calls, and a short warmup measures the ramp.
 
 value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
-with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).
+with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).  For
+a backward workload `fwd_bwd_step` adds the backward's 10 * D * H * sum_b S * K_b
+to the count over the same step time.
 The attention-forward call (the V-to-FP16 tile pass and the attention kernel,
 launched back to back on one stream) is also timed alone with HIP events on
 the launch stream; that time gives the roofline fraction against the MI355X
@@ -210,6 +212,9 @@ def main():
         bflops = wl.bwd_flops()
         out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
                            "algorithmic_flops": bflops}
+        # the whole step (prologues, forward, backward) against forward + backward FLOPs
+        out["fwd_bwd_step"] = {"ms": round(ms_step, 4), "flops": fwd_flops + bflops,
+                               "tflops": round((fwd_flops + bflops) / (ms_step * 1e-3) / 1e12, 2)}
 
     if args.block_steps > 0:
         out["blocks"] = bench_blocks(qi, torch, np, wl, geo, qp, kp, g["v"], args.block_steps, fwd_ms)

@@ -330,7 +330,12 @@ size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
  *                  BF16 O would shift D by ~2^-9 |dO||O| sqrt(128), more than
  *                  the gain gradients tolerate.
  *   lse            FP32 dense [B,H,S] from the forward.
- *   d_o            BF16 [B,S,H,128] upstream gradient.
+ *   d_o            BF16 [B,S,H,128] upstream gradient.  The dv product
+ *                  takes it as FP16 of dO * 2^e, one power of two per
+ *                  (sample, head) that puts the slice's largest |dO| in
+ *                  [2^14, 2^15): elements below 2^-28 of that maximum keep an
+ *                  absolute error under 2^-39 of it; the scale is undone
+ *                  exactly, so dv stays linear in power-of-two factors of dO.
  *   gain_q, gain_k FP32 device [gain_streams][128].
  *   dq, dk, dv     FP32 [B,S,H,128] outputs (dq, dk w.r.t. q_raw, k_raw).
  *   dgain_q_ps, dgain_k_ps   FP32 device [B][gain_streams][128]: gain
@@ -339,8 +344,8 @@ size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
  *                  per-sample values summed in ascending b.
  *   workspace      device buffer of at least qi_joint_attn_bwd_workspace()
  *                  bytes, 256-byte aligned; its contents are scratch.
- * The sequence strides of q, k, v and d_o must stay below 2^26 elements
- * (QI_E_UNSUPPORTED otherwise).
+ * The sequence strides of q, k, v and d_o must stay below 2^26 elements, and
+ * H at most 65535 (QI_E_UNSUPPORTED otherwise).
  */
 int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd q,
                       qi_bshd k, qi_bshd v, qi_bshd o_f32, const float* lse, qi_bshd d_o,

@@ -219,7 +219,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dvec, pq, pk, total;
+  size_t dvec, pq, pk, do16, amax, scale, total;
   int n_txt_chunks, n_chunks;
 };
 
@@ -319,7 +319,11 @@ BwdLayout bwd_layout(const qi_geom* g) {
   L.pq = align256((size_t)g->B * g->H * S * 4);
   const size_t part = align256((size_t)g->B * L.n_chunks * kHeadDim * 4);
   L.pk = L.pq + part;
-  L.total = L.pk + part;
+  L.do16 = L.pk + part;
+  L.amax = L.do16 + align256((size_t)g->B * S * g->H * kHeadDim * 2);
+  const size_t n_qtiles = (size_t)ceil_div(S, kBwdDqWaves * 32);
+  L.scale = L.amax + align256((size_t)g->B * g->H * n_qtiles * kBwdDqWaves * 4);
+  L.total = L.scale + align256((size_t)g->B * g->H * 4);
   return L;
 }
 
@@ -796,10 +800,14 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
   if (S > 1 && (k.ss > kFwdMaxRowStride || v.ss > kFwdMaxRowStride || q.ss > kFwdMaxRowStride ||
                 d_o.ss > kFwdMaxRowStride))
     return fail(QI_E_UNSUPPORTED, "q/k/v/d_o sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if (geom->H > 65535) return fail(QI_E_UNSUPPORTED, "H=%d above the 65535 heads the backward launches", geom->H);
   if ((rc = current_device_gate())) return rc;
 
   char* ws = (char*)workspace;
   float* Dvec = (float*)(ws + Lw.dvec);
+  uint16_t* do16 = (uint16_t*)(ws + Lw.do16);
+  uint32_t* amax = (uint32_t*)(ws + Lw.amax);
+  float* inv_scale = (float*)(ws + Lw.scale);
   const int rows_per_wg = kBwdDqWaves * 32;
   const int keys_per_wg = kBwdKvWaves * 32;
   int nk_max = 0;
@@ -811,6 +819,9 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.v = view_of<const uint16_t>(v, b0);
     a.o = view_of<const float>(o_f32, b0);
     a.dO = view_of<const uint16_t>(d_o, b0);
+    a.do16 = View<const uint16_t>{do16 + (int64_t)b0 * S * geom->H * kHeadDim, S * geom->H * kHeadDim,
+                                  (int64_t)geom->H * kHeadDim, kHeadDim};
+    a.do_inv_scale = inv_scale + (int64_t)b0 * geom->H;
     a.lse = lse + (int64_t)b0 * geom->H * S;
     a.Dvec = Dvec + (int64_t)b0 * geom->H * S;
     a.dq = view_of<float>(dq, b0);
@@ -822,6 +833,7 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.T_txt = geom->T_txt;
     a.T_img = geom->grid_h * geom->grid_w;
     a.n_qtiles = (int)ceil_div(S, rows_per_wg);
+    a.do_amax = amax + (int64_t)b0 * geom->H * a.n_qtiles * kBwdDqWaves;
     nk_max = 0;
     for (int i = 0; i < nb; ++i) {
       const int L = geom->txt_len[b0 + i];
@@ -835,6 +847,19 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(kBwdDqWaves * 64), 0,
                        stream, a);
     if ((rc = launched("attn_bwd_dq_kernel"))) return rc;
+    {  // dO -> FP16 under the per-(b, h) scale, from the maxima the dQ pass recorded
+      DoPrepArgs pa;
+      pa.dO = a.dO;
+      pa.out = const_cast<uint16_t*>(a.do16.p);
+      pa.amax = a.do_amax;
+      pa.n_amax = a.n_qtiles * kBwdDqWaves;
+      pa.inv_scale = inv_scale + (int64_t)b0 * geom->H;
+      pa.S = (int)S;
+      pa.H = geom->H;
+      hipLaunchKernelGGL(do_convert_kernel, dim3((unsigned)ceil_div(S, kDoConvRows), (unsigned)geom->H, (unsigned)nb),
+                         dim3(256), 0, stream, pa);
+      if ((rc = launched("do_convert_kernel"))) return rc;
+    }
     const dim3 kv_grid((unsigned)((int64_t)nb * geom->H * a.n_ktiles));
     hipLaunchKernelGGL(attn_bwd_dk_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
     if ((rc = launched("attn_bwd_dk_kernel"))) return rc;
@@ -850,15 +875,15 @@ const char* qi_trace(void) {
   static const std::string s = [] {
     char buf[4096];
     snprintf(buf, sizeof buf,
-             "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":2,"
+             "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":3,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
              "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
              "\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\","
              "\"qkv_proj\":\"proj_gemm_kernel\",\"out_proj\":\"proj_gemm_kernel\",\"rope_table\":\"rope_table_kernel\","
              "\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
-             "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\"},"
-             "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","
+             "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\",\"bwd_do_prep\":\"do_convert_kernel\"},"
+             "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V and bwd dV: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","
              "\"frozen\":{\"fwd_key_tile\":%d,\"bwd_dq_key_tile\":%d,\"bwd_dkdv_query_tile\":%d,"
              "\"prologue_dgain_chunk\":%d,\"key_order\":\"text tiles from 0, image tiles from T_txt\","
              "\"bwd_query_order\":\"valid text, image, padded text\","
@@ -867,7 +892,7 @@ const char* qi_trace(void) {
              "\"bwd_D\":\"rowsum(dO*O) from the fp32 forward O\","
              "\"reference_max_threshold_log2\":8,"
              "\"ds_split\":\"hi=bf16(dS), lo=bf16(dS-hi), accumulated hi then lo (dQ, dK)\","
-             "\"dv_p_split\":\"hi=bf16(P), lo=bf16(P-hi), accumulated hi then lo\","
+             "\"dv_operands\":\"P fp16 RNE, dO fp16 RNE of dO*2^e per (b,h) (e from its max|dO|, taken in the dQ pass), dV=acc*2^-e\","
              "\"rms_sum_tree\":\"8 sequential per lane, xor 8,4,2,1\","
              "\"dgain_fold\":\"chunks ascending per sample, then samples ascending\"},"
              "\"free\":[\"rows per workgroup\",\"grid order / XCD mapping\",\"LDS layout\",\"prefetch depth\"],"

@@ -38,6 +38,7 @@
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_lds.h"
+#include "qi_attn_contract.h"
 
 namespace qi {
 
@@ -144,7 +145,7 @@ __device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
   }
 }
 
-template <bool kAcc, bool kS, bool kDp, int k>
+template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
 __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
   using P = Plan<kAcc, kS, kDp>;
   if constexpr (k < P::n) {
@@ -154,10 +155,16 @@ __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
     if constexpr (k < P::nacc) {
       constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
-      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d0]);
-      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d1]);
-      st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d0]);
-      st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
+      if constexpr (kF16) {  // FP16 operands, one product
+        using attn::f16x8;
+        st.acc[d0] = attn::mfma32h(__builtin_bit_cast(f16x8, x[0]), __builtin_bit_cast(f16x8, st.dh[c2]), st.acc[d0]);
+        st.acc[d1] = attn::mfma32h(__builtin_bit_cast(f16x8, x[1]), __builtin_bit_cast(f16x8, st.dh[c2]), st.acc[d1]);
+      } else {
+        st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d0]);
+        st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dh[c2]), st.acc[d1]);
+        st.acc[d0] = mfma32(x[0], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d0]);
+        st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
+      }
     } else if constexpr (kDp) {
       constexpr int j = k - P::nacc, kk = j >> 1, kb = j & 1;
       st.s[kb] = mfma32(x[0], st.b1[kk], st.s[kb]);
@@ -168,7 +175,7 @@ __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
       st.s[1] = mfma32(x[1], st.b1[kk], st.s[1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    g_step<kAcc, kS, kDp, k + 1>(st, f, b);
+    g_step<kAcc, kS, kDp, kF16, k + 1>(st, f, b);
   }
 }
 
@@ -180,7 +187,7 @@ __device__ __forceinline__ void g_prefetch(Ring& f, const GBases& b) {
   }
 }
 
-template <bool kAcc, bool kS, bool kDp>
+template <bool kAcc, bool kS, bool kDp, bool kF16 = false>
 __device__ __forceinline__ void g_matrix(GState& st, GBases b) {
   if (kS) {
 #pragma unroll
@@ -198,7 +205,7 @@ __device__ __forceinline__ void g_matrix(GState& st, GBases b) {
   __builtin_amdgcn_sched_barrier(0);
   g_prefetch<kAcc, kS, kDp, 0>(f, b);
   __builtin_amdgcn_sched_barrier(0);
-  g_step<kAcc, kS, kDp, 0>(st, f, b);
+  g_step<kAcc, kS, kDp, kF16, 0>(st, f, b);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -255,6 +262,7 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
 
   GState st;
   float dpart = 0.f;
+  uint32_t amax = 0;  // max |dO| of this lane's values, as BF16 magnitude bits (ordered like the values)
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
@@ -276,9 +284,14 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
       dpart = dpart + p0;
       const float p1 = bf16_hi(zd[w]) * ov[2 * w + 1];
       dpart = dpart + p1;
+      amax = max(amax, max(zd[w] & 0x7fffu, (zd[w] >> 16) & 0x7fffu));
     }
   }
   st.D = dpart + __shfl_xor(dpart, 32);
+  // this wave's max |dO| (order-free) for the dV operand's scale
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+  if (lane == 0) a.do_amax[(((int64_t)b * a.H + h) * a.n_qtiles + qt) * kBwdDqWaves + wave] = amax;
   st.lse2 = INFINITY;
   if (qvalid) {
     const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
@@ -409,7 +422,8 @@ struct QTiles {
 
 // P = exp2(s*c - LSE*log2 e) and, for dK, dS = P (dP - D), per query row
 // (register r of block qb holds query 32*qb + 8*(r/4) + 4*hh + r%4); rows
-// past the tile's valid count are exactly 0.  Split hi/lo per 16-row chunk.
+// past the tile's valid count are exactly 0.  dS is split hi/lo per 16-row
+// chunk; P (dV) is rounded once to FP16.
 template <bool kDk>
 __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const float* dd, int nq, int hh) {
 #pragma unroll
@@ -432,10 +446,16 @@ __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const f
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      uint32_t hi[4], lo[4];
-      split_pack(x + 8 * half, hi, lo);
-      st.dh[2 * qb + half] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-      st.dl[2 * qb + half] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      if constexpr (kDk) {
+        uint32_t hi[4], lo[4];
+        split_pack(x + 8 * half, hi, lo);
+        st.dh[2 * qb + half] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        st.dl[2 * qb + half] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      } else {  // dV: P in FP16 (RNE), one operand
+        const float* v = x + 8 * half;
+        st.dh[2 * qb + half] = u32x4{attn::pack_f16x2(v[0], v[1]), attn::pack_f16x2(v[2], v[3]),
+                                     attn::pack_f16x2(v[4], v[5]), attn::pack_f16x2(v[6], v[7])};
+      }
     }
   }
 }
@@ -520,7 +540,9 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
   };
   // each group loads only one of Q and dO: group 0 dO (dK) or Q (dV)
   const bool loads_o = (grp == 0) == kDk;
-  const RowOff ro = row_offsets(loads_o ? a.dO.ss : a.q.ss, lane);
+  // dO: BF16 for dP (dK); FP16 dO * 2^e for the dV product
+  const View<const uint16_t> dO = kDk ? a.dO : a.do16;
+  const RowOff ro = row_offsets(loads_o ? dO.ss : a.q.ss, lane);
   const int64_t hb = ((int64_t)b * a.H + h) * a.S;  // [b, h] row of LSE and D
   auto load_q = [&](int j) {
     int q0, nq;
@@ -531,7 +553,7 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
   auto load_o = [&](int j) {
     int q0, nq;
     qt.bounds(j, q0, nq);
-    load_rows(a.dO, ro, obuf(j), b, h, q0, nq, sub, lane);
+    load_rows(dO, ro, obuf(j), b, h, q0, nq, sub, lane);
     if (kDk && sub == 0 && lane < nq) dma4((const char*)(a.Dvec + hb + q0), 4u * lane, addr_of((const char*)drow(j)));
   };
   auto load_tile = [&](int j) {
@@ -568,27 +590,25 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
     if (t + 2 < nt) load_tile(t + 2);
     kv_softmax<kDk>(st, lrow(t), drow(t), nq_of(t), hh);
     bar();
-    g_matrix<true, true, kDk>(st, bases(t, true));
+    g_matrix<true, true, kDk, !kDk>(st, bases(t, true));
     __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
     bar();
   }
   kv_softmax<kDk>(st, lrow(nt - 1), drow(nt - 1), nq_of(nt - 1), hh);
   bar();
-  g_matrix<true, false, kDk>(st, bases(nt - 1, false));
+  g_matrix<true, false, kDk, !kDk>(st, bases(nt - 1, false));
   if (grp == 0) bar();
 
   if (kvalid) {
+    // dK: times 1/sqrt(128); dV: times 2^-e, undoing dO's power-of-two scale (exact)
+    const float f = kDk ? kScale : a.do_inv_scale[(int64_t)b * a.H + h];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        if (kDk)
-          *(f32x4*)(out + d0) = f32x4{st.acc[d][4 * g4] * kScale, st.acc[d][4 * g4 + 1] * kScale,
-                                      st.acc[d][4 * g4 + 2] * kScale, st.acc[d][4 * g4 + 3] * kScale};
-        else
-          *(f32x4*)(out + d0) = f32x4{st.acc[d][4 * g4], st.acc[d][4 * g4 + 1], st.acc[d][4 * g4 + 2],
-                                      st.acc[d][4 * g4 + 3]};
+        *(f32x4*)(out + d0) = f32x4{st.acc[d][4 * g4] * f, st.acc[d][4 * g4 + 1] * f, st.acc[d][4 * g4 + 2] * f,
+                                    st.acc[d][4 * g4 + 3] * f};
       }
   }
 }
@@ -598,6 +618,43 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
 __global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
   kv_pass<true>(a, smem);
+}
+
+// dO for the dV product: FP16 of dO * 2^e with one power of two per (sample,
+// head), chosen from that slice's max |dO| so that its largest element lands
+// in [2^14, 2^15) (e at most 100).  The scaling is exact and the conversion
+// rounds to nearest even: relative error <= 2^-11 for |dO| >= max|dO| * 2^-28,
+// absolute error <= max|dO| * 2^-39 below (e under its cap).  The maximum is order-free and
+// covers only the slice's own rows, so the scale, like every output bit,
+// depends on nothing outside the (sample, head).
+__global__ __launch_bounds__(256) void do_convert_kernel(DoPrepArgs a) {
+  __shared__ uint32_t red[4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H + h;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < a.n_amax; i += 256) m = max(m, a.amax[bh * a.n_amax + i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  int e = 0;  // max |dO| = f * 2^E with f in [0.5, 1): scale by 2^(15 - E)
+  if (m != 0u && m < 0x7f80u) {  // nonzero and finite
+    int E;
+    (void)frexpf(__uint_as_float(m << 16), &E);
+    e = min(15 - E, 100);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.inv_scale[bh] = ldexpf(1.0f, -e);
+  const int r0 = blockIdx.x * kDoConvRows;
+  for (int i = threadIdx.x; i < kDoConvRows * 16; i += 256) {  // 16 chunks of 8 channels per row
+    const int s_ = r0 + (i >> 4), c = i & 15;
+    if (s_ >= a.S) break;
+    const u32x4 v = *(const u32x4*)(a.dO.row(b, s_, h) + 8 * c);
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = attn::pack_f16x2(ldexpf(bf16_lo(v[k]), e), ldexpf(bf16_hi(v[k]), e));
+    *(u32x4*)(a.out + (((int64_t)b * a.S + s_) * a.H + h) * kHeadDim + 8 * c) = o;
+  }
 }
 
 __global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dv_kernel(BwdArgs a) {

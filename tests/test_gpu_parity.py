@@ -208,6 +208,56 @@ def test_backward_small(orc, spec, streams):
         assert not r["dv"][b, L:wl.T_txt].any() and not r["dk"][b, L:wl.T_txt].any()
 
 
+def _bits_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+def test_backward_exactly_linear_in_dO():
+    """Every gradient is linear in dO, and the path's arithmetic keeps that
+    exact for power-of-two factors: gradients of dO * 2^k are the gradients
+    of dO times 2^k, bit for bit (k = -16 and +12 move dO far from unit
+    scale; the dV operand's internal scaling must follow).  dO = 0 gives
+    exactly zero everywhere."""
+    wl = small_wl(BWD_SMALL[4], backward=True)  # multi_tile
+    inp, g = gpu_inputs(wl, gain_streams=2)
+    geo = geom_of(wl, gain_streams=2)
+    q, k, o, lse, r0 = _bwd_all(g, geo)
+    for kexp in (-16, 12):
+        gs = dict(g, dO=(g["dO"].float() * 2.0 ** kexp).to(torch.bfloat16))
+        _, _, _, _, rs = _bwd_all(gs, geo)
+        for name, t in r0.items():
+            assert _bits_equal(rs[name], t * 2.0 ** kexp), f"{name} at dO * 2^{kexp}"
+    gz = dict(g, dO=torch.zeros_like(g["dO"]))
+    _, _, _, _, rz = _bwd_all(gz, geo)
+    for name, t in rz.items():
+        assert not t.any(), f"{name} with dO = 0"
+    # one (sample, head) slice of dO scaled by 2^-24: that slice's dq, dk, dv
+    # scale exactly, and every other slice keeps its bits
+    d1 = g["dO"].clone()
+    d1[1, :, 0] = (d1[1, :, 0].float() * 2.0 ** -24).to(torch.bfloat16)
+    _, _, _, _, r1 = _bwd_all(dict(g, dO=d1), geo)
+    for name in ("dq", "dk", "dv"):
+        a, ref = r1[name], r0[name]
+        assert _bits_equal(a[1, :, 0], ref[1, :, 0] * 2.0 ** -24), f"{name} of the scaled slice"
+        assert _bits_equal(a[0], ref[0]) and _bits_equal(a[1, :, 1:], ref[1, :, 1:]), f"{name} of other slices"
+
+
+def test_backward_wide_channel_range_dv(orc):
+    """dO channels spread over 2^-12 .. 2^12: each dV channel, divided by its
+    channel's factor, stays within the bound of the oracle's (the dV operand
+    shares one scale per (sample, head), set by that slice's largest
+    element)."""
+    wl = small_wl(BWD_SMALL[4], seed=105, backward=True)
+    inp, g = gpu_inputs(wl)
+    geo = geom_of(wl)
+    s = 2.0 ** torch.linspace(-12, 12, 128).round()
+    dO = (inp["dO"].float() * s).to(torch.bfloat16)
+    q, k, o, lse, r = _bwd_all(dict(g, dO=dO.to(DEV)), geo)
+    dqp, dkp, dv = orc.attn_bwd(f64(q), f64(k), f64(inp["v"].float()), f64(dO.float()), wl.txt_len, wl.T_txt)
+    sn = s.double().numpy()
+    mixed_check(f64(r["dv"]) / sn, dv / sn, "dv per channel")
+
+
 def test_backward_full_sampled_head(orc):
     wl = workloads.WORKLOADS["1024sq_bwd"]
     inp, g = gpu_inputs(wl)
