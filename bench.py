@@ -3,9 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024sq]
 
 A step is one pass of the path over one batch of synthetic input that is
-already resident in HBM: the Q and K prologues (RMSNorm + gain + RoPE) and
-the attention forward; for a backward workload the step also runs the
-backward (attention + prologue gradients).  Prints ONE JSON line.
+already resident in HBM: the Q and K prologues (RMSNorm + gain + RoPE), the
+conversion of V to the attention's FP16 key tiles, and the attention
+forward; for a backward workload the step also runs the backward (attention
++ prologue gradients).  Prints ONE JSON line.
+
+By default a step is two library calls: qi_qkv_prologue (Q and K prologues
+and the V conversion in one launch) and qi_joint_attn_fwd_vtiles (the
+attention kernel alone); --separate-prologue runs qi_qknorm_rope twice and
+qi_joint_attn_fwd (V conversion + attention) instead.  Both give the same
+bytes.
 
 By default every call is launched from the host each step; --graph captures
 each part of a step (prologues, forward call, backward call) once as a HIP
@@ -17,9 +24,10 @@ value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
 with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).  For
 a backward workload `fwd_bwd_step` adds the backward's 10 * D * H * sum_b S * K_b
 to the count over the same step time.
-The attention-forward call (the V-to-FP16 tile pass and the attention kernel,
-launched back to back on one stream) is also timed alone with HIP events on
-the launch stream; that time gives the roofline fraction against the MI355X
+The attention-forward call is also timed alone with HIP events on the
+launch stream (by default one launch of the attention kernel; with
+--separate-prologue the V tile pass and the attention kernel back to back);
+that time gives the roofline fraction against the MI355X
 dense BF16 MFMA peak (2.5 PFLOP/s).  The CPU oracle is timed on a bounded
 sample of the same workload on the host cores (cpu_baseline).
 """
@@ -51,6 +59,9 @@ def parse():
     ap.add_argument("--workload", default="1024sq")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--separate-prologue", action="store_true",
+                    help="run the step as qi_qknorm_rope twice + qi_joint_attn_fwd (V converted inside the forward "
+                         "call) instead of qi_qkv_prologue + qi_joint_attn_fwd_vtiles")
     ap.add_argument("--graph", action="store_true",
                     help="replay each part of a step from a captured HIP graph instead of launching every call")
     ap.add_argument("--proj-steps", type=int, default=50,
@@ -115,12 +126,20 @@ def main():
         grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
 
     # the parts of a step, each a fixed sequence of library calls
-    def pro():
-        qi.qknorm_rope(g["q"], g["g_q"], geo, out=qp)
-        qi.qknorm_rope(g["k"], g["g_k"], geo, out=kp)
+    if args.separate_prologue:
+        def pro():
+            qi.qknorm_rope(g["q"], g["g_q"], geo, out=qp)
+            qi.qknorm_rope(g["k"], g["g_k"], geo, out=kp)
 
-    def fwd():
-        qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of, workspace=fws)
+        def fwd():
+            qi.joint_attn_fwd(qp, kp, g["v"], geo, out=o, lse=lse, out_f32=of, workspace=fws)
+    else:
+        # one launch for the Q/K prologues and the V tile conversion, then the attention kernel alone
+        def pro():
+            qi.qkv_prologue(g["q"], g["k"], g["v"], g["g_q"], g["g_k"], geo, q=qp, k=kp, v_tiles=fws)
+
+        def fwd():
+            qi.joint_attn_fwd_vtiles(qp, kp, fws, geo, out=o, lse=lse, out_f32=of)
 
     def bwd():
         qi.joint_attn_bwd(g["q"], g["k"], qp, kp, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo,
@@ -176,10 +195,19 @@ def main():
     value = fwd_flops / (ms_step * 1e-3) / 1e12
     attn_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     pro_bytes = 2 * 2 * 2 * wl.B * wl.S * wl.H * 128  # Q and K, read + write BF16
+    if not args.separate_prologue:
+        # + the valid V rows read and the FP16 key tiles written (64 keys x 128 channels x 2 B each)
+        for L in wl.txt_len:
+            pro_bytes += (L + wl.T_img) * wl.H * 128 * 2 + (-(-L // 64) + -(-wl.T_img // 64)) * wl.H * 64 * 128 * 2
 
-    # one forward call = v_tiles_kernel (V to FP16 key tiles) + attn_fwd_kernel, timed together on the launch stream
-    traffic = traffic_from_profile("attn_fwd_call", "qi_attn_fwd.hip", args.workload)
-    roofline = {"bound": "mfma", "kernel": "attn_fwd_kernel (+ v_tiles_kernel: one forward call)",
+    if args.separate_prologue:
+        # one forward call = v_tiles_kernel (V to FP16 key tiles) + attn_fwd_kernel, timed together
+        traffic = traffic_from_profile("attn_fwd_call", "qi_attn_fwd.hip", args.workload)
+        kernel = "attn_fwd_kernel (+ v_tiles_kernel: one forward call)"
+    else:
+        traffic = traffic_from_profile("attn_fwd_kernel", "qi_attn_fwd.hip", args.workload)
+        kernel = "attn_fwd_kernel (one qi_joint_attn_fwd_vtiles call)"
+    roofline = {"bound": "mfma", "kernel": kernel,
                 "achieved": round(attn_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "flops_per_launch": fwd_flops, "avg_launch_ms": round(fwd_ms, 4)}
@@ -203,8 +231,9 @@ def main():
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "attn_fwd": {"ms": round(fwd_ms, 4), "tflops": round(attn_tflops, 2),
                      "pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2)},
-        "prologue_qk": {"ms": round(pro_ms, 4), "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
-                        "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "prologue": {"calls": "qi_qknorm_rope x 2" if args.separate_prologue else "qi_qkv_prologue (Q, K, V tiles)",
+                     "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "launch": "hip_graph_replay" if args.graph else "eager",
     }

@@ -145,6 +145,35 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
                       hipStream_t stream);
 
 /*
+ * qi_qkv_prologue -- the forward's preparation in one launch: the Q and K
+ * prologues of qi_qknorm_rope (same arithmetic, same bytes) and the V ->
+ * FP16 key-tile conversion that qi_joint_attn_fwd otherwise runs first.
+ * ([Kernel list] rows qk_rmsnorm, multi_axis_rope and joint_attn_av_gemm;
+ * [Roadmap] "Numerical requirements": a fused kernel gives the bytes of the
+ * unfused ones.)
+ *   q_raw, k_raw  BF16 [B,S,H,128] inputs; v BF16 [B,S,H,128].
+ *   gain_q, gain_k  FP32 device [gain_streams][128].
+ *   q, k     BF16 [B,S,H,128] outputs q', k'.
+ *   v_tiles  device buffer of at least qi_joint_attn_fwd_workspace() bytes,
+ *            256-byte aligned: receives V as FP16 v * 2^-8 transposed key
+ *            tiles, the format qi_joint_attn_fwd_vtiles reads.
+ */
+int qi_qkv_prologue(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd v,
+                    const float* gain_q, const float* gain_k, qi_bshd q, qi_bshd k,
+                    void* v_tiles, size_t v_tiles_bytes, hipStream_t stream);
+
+/*
+ * qi_joint_attn_fwd_vtiles -- qi_joint_attn_fwd with V already converted:
+ * one attention launch over the key tiles that qi_qkv_prologue wrote for
+ * the same geometry and V (the contents are not checked).  O, LSE and O_f32
+ * equal qi_joint_attn_fwd's byte for byte.  Arguments and errors as for
+ * qi_joint_attn_fwd, with v_tiles (read only) in place of v and workspace.
+ */
+int qi_joint_attn_fwd_vtiles(const qi_geom* geom, qi_bshd q, qi_bshd k, const void* v_tiles,
+                             size_t v_tiles_bytes, qi_bshd o, float* lse, float* o_f32,
+                             hipStream_t stream);
+
+/*
  * Key-block forward and merge -- the ring-ready form of qi_joint_attn_fwd
  * ([Kernel list], row joint_attention_fused, which is marked for Ulysses /
  * Ring sequence parallelism; [Roadmap], "Numerical requirements": distributed

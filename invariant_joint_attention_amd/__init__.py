@@ -22,7 +22,8 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
           5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
 
 # every entry point declared in include/qi.h
-SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial",
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_qkv_prologue",
+           "qi_joint_attn_fwd_vtiles", "qi_joint_attn_fwd_partial",
            "qi_joint_attn_merge", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
            "qi_joint_attn_key_slots",
            "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd_workspace.argtypes = [G]
         L.qi_joint_attn_fwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
+        L.qi_qkv_prologue.argtypes = [G, QiBshd, QiBshd, QiBshd, P, P, QiBshd, QiBshd, P, ctypes.c_size_t, S]
+        L.qi_joint_attn_fwd_vtiles.argtypes = [G, QiBshd, QiBshd, P, ctypes.c_size_t, QiBshd, P, P, S]
         L.qi_joint_attn_fwd_partial.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_merge.argtypes = [G, ctypes.c_int32, P, P, P, QiBshd, P, P, S]
         L.qi_qkv_proj_workspace.argtypes = [G]
@@ -168,6 +171,33 @@ def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None, wo
     _check(lib().qi_joint_attn_fwd(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
                                    _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream()))
+    return out, lse
+
+
+def qkv_prologue(q_raw, k_raw, v, gain_q, gain_k, geom: Geometry, q=None, k=None, v_tiles=None):
+    """Q and K prologues and the V tile conversion in one launch; returns
+    (q', k', v_tiles) with v_tiles a device byte tensor of
+    ``fwd_workspace_bytes`` holding V in the attention's FP16 tile format."""
+    q = _empty(q_raw.shape, torch.bfloat16, q_raw) if q is None else q
+    k = _empty(k_raw.shape, torch.bfloat16, k_raw) if k is None else k
+    if v_tiles is None:
+        v_tiles = _empty((max(1, fwd_workspace_bytes(geom)),), torch.uint8, q_raw)
+    _check(lib().qi_qkv_prologue(geom.ptr(), _bshd(q_raw), _bshd(k_raw), _bshd(v), _ptr(gain_q), _ptr(gain_k),
+                                 _bshd(q), _bshd(k), _ptr(v_tiles), v_tiles.numel() * v_tiles.element_size(),
+                                 _stream()))
+    return q, k, v_tiles
+
+
+def joint_attn_fwd_vtiles(q, k, v_tiles, geom: Geometry, out=None, lse=None, out_f32=None):
+    """Attention forward over the V tiles written by ``qkv_prologue``;
+    returns (O, LSE) as ``joint_attn_fwd``."""
+    if out is None:
+        out = _empty(q.shape, torch.bfloat16, q)
+    if lse is None:
+        lse = _empty((geom.B, geom.H, geom.S), torch.float32, q)
+    _check(lib().qi_joint_attn_fwd_vtiles(geom.ptr(), _bshd(q), _bshd(k), _ptr(v_tiles),
+                                          v_tiles.numel() * v_tiles.element_size(), _bshd(out), _ptr(lse),
+                                          _ptr(out_f32), _stream()))
     return out, lse
 
 

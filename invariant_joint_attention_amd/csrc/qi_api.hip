@@ -331,7 +331,8 @@ BwdLayout bwd_layout(const qi_geom* g) {
 // With blk the partial kernel runs over that key block and writes the row
 // state (acc, m, l) instead of O and LSE.
 int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_p, float* lse, float* o_f32,
-               uint16_t* vt, const qi_key_block* blk, float* pacc, float* pm, float* pl, hipStream_t stream) {
+               uint16_t* vt, const qi_key_block* blk, float* pacc, float* pm, float* pl, hipStream_t stream,
+               bool vt_ready = false) {
   int rc;
   const int64_t S = seq_len(geom);
   // vt: FP16 V^T key tiles [B][H][nt_max][128][64] in the workspace
@@ -374,9 +375,11 @@ int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_
     c.with_text = a.blk_text;
     c.img_t0 = blk ? a.blk_img_t0 : 0;
     c.img_t1 = blk ? a.blk_img_t1 : nt_max;
-    hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0, stream,
-                       c);
-    if ((rc = launched("v_tiles_kernel"))) return rc;
+    if (!vt_ready) {
+      hipLaunchKernelGGL(v_tiles_kernel, dim3((unsigned)nt_max, (unsigned)geom->H, (unsigned)nb), dim3(256), 0,
+                         stream, c);
+      if ((rc = launched("v_tiles_kernel"))) return rc;
+    }
 
     const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
     if (blk) {
@@ -388,6 +391,24 @@ int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_
     }
   }
   return QI_OK;
+}
+
+PrologueArgs prologue_args(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd y, float* yf, int b0, int nb) {
+  PrologueArgs a;
+  a.x = view_of<const uint16_t>(x, b0);
+  a.y = view_of<uint16_t>(y, b0);
+  a.yf = yf;
+  a.gain = gain;
+  a.gain_streams = g->gain_streams;
+  a.B = nb;
+  a.S = (int)seq_len(g);
+  a.H = g->H;
+  a.T_txt = g->T_txt;
+  a.gh = g->grid_h;
+  a.gw = g->grid_w;
+  a.theta = g->rope_theta;
+  a.eps = g->rms_eps;
+  return a;
 }
 
 int launch_prologue(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd y, float* yf, hipStream_t st) {
@@ -503,6 +524,82 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   if ((rc = current_device_gate())) return rc;
 
   return launch_fwd(geom, q, k, v, &o, lse, o_f32, (uint16_t*)workspace, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int qi_qkv_prologue(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd v, const float* gain_q,
+                    const float* gain_k, qi_bshd q, qi_bshd k, void* v_tiles, size_t v_tiles_bytes,
+                    hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t gbytes = (int64_t)geom->gain_streams * kHeadDim * 4;
+  if ((rc = check_view(geom, q_raw, 2, false, "q_raw", ext))) return rc;
+  if ((rc = check_view(geom, k_raw, 2, false, "k_raw", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_dense(gain_q, gbytes, false, "gain_q", ext))) return rc;
+  if ((rc = check_dense(gain_k, gbytes, false, "gain_k", ext))) return rc;
+  if ((rc = check_view(geom, q, 2, true, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, true, "k", ext))) return rc;
+  const size_t vt_need = fwd_workspace_bytes(geom);
+  if (!v_tiles) return fail(QI_E_WORKSPACE, "v_tiles is null");
+  if ((uintptr_t)v_tiles % 256) return fail(QI_E_ALIGN, "v_tiles is not 256-byte aligned");
+  if (v_tiles_bytes < vt_need)
+    return fail(QI_E_WORKSPACE, "v_tiles of %zu bytes is smaller than the %zu required", v_tiles_bytes, vt_need);
+  ext.push_back({"v_tiles", (uintptr_t)v_tiles, (uintptr_t)v_tiles + vt_need, true});
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+
+  const int nt_max = fwd_nt_max(geom);
+  for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
+    const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
+    QkvPrologueArgs a;
+    a.q = prologue_args(geom, q_raw, gain_q, q, nullptr, b0, nb);
+    a.k = prologue_args(geom, k_raw, gain_k, k, nullptr, b0, nb);
+    a.nblk = ceil_div((int64_t)nb * S, 4);
+    a.v.v = view_of<const uint16_t>(v, b0);
+    a.v.out = (uint16_t*)v_tiles + (int64_t)b0 * geom->H * nt_max * kVtileElems;
+    a.v.H = geom->H;
+    a.v.T_txt = geom->T_txt;
+    a.v.T_img = geom->grid_h * geom->grid_w;
+    a.v.nt_max = nt_max;
+    for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.v.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
+    a.v.with_text = 1;
+    a.v.img_t0 = 0;
+    a.v.img_t1 = nt_max;
+    const int64_t grid = 2 * a.nblk + (int64_t)nt_max * geom->H * nb;
+    if (grid > 0x7fffffff) return fail(QI_E_UNSUPPORTED, "%lld workgroups in one prologue launch", (long long)grid);
+    hipLaunchKernelGGL(qkv_prologue_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    if ((rc = launched("qkv_prologue_kernel"))) return rc;
+  }
+  return QI_OK;
+}
+
+int qi_joint_attn_fwd_vtiles(const qi_geom* geom, qi_bshd q, qi_bshd k, const void* v_tiles, size_t v_tiles_bytes,
+                             qi_bshd o, float* lse, float* o_f32, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  std::vector<Extent> ext;
+  const int64_t S = seq_len(geom);
+  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+  if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
+  if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  const size_t vt_need = fwd_workspace_bytes(geom);
+  if (!v_tiles) return fail(QI_E_WORKSPACE, "v_tiles is null");
+  if ((uintptr_t)v_tiles % 256) return fail(QI_E_ALIGN, "v_tiles is not 256-byte aligned");
+  if (v_tiles_bytes < vt_need)
+    return fail(QI_E_WORKSPACE, "v_tiles of %zu bytes is smaller than the %zu required", v_tiles_bytes, vt_need);
+  ext.push_back({"v_tiles", (uintptr_t)v_tiles, (uintptr_t)v_tiles + vt_need, false});
+  if ((rc = check_alias(ext))) return rc;
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if ((rc = current_device_gate())) return rc;
+  const qi_bshd no_v{nullptr, 0, 0, 0};
+  return launch_fwd(geom, q, k, no_v, &o, lse, o_f32, (uint16_t*)v_tiles, nullptr, nullptr, nullptr, nullptr, stream,
+                    true);
 }
 
 int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_key_block blk, float* acc,
@@ -877,7 +974,8 @@ const char* qi_trace(void) {
     snprintf(buf, sizeof buf,
              "{\"library\":\"qi\",\"target\":\"gfx950\",\"contract_version\":3,"
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
-             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
+             "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\","
+             "\"qkv_prologue\":\"qkv_prologue_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
              "\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\","
              "\"qkv_proj\":\"proj_gemm_kernel\",\"out_proj\":\"proj_gemm_kernel\",\"rope_table\":\"rope_table_kernel\","
              "\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","

@@ -121,6 +121,14 @@ struct VtileArgs {
 };
 __global__ void v_tiles_kernel(VtileArgs a);
 
+// The forward's Q and K prologues and its V tile conversion in one launch.
+struct QkvPrologueArgs {
+  PrologueArgs q, k;  // same token range (B of this launch)
+  VtileArgs v;
+  int64_t nblk;       // blocks per prologue: ceil(B * S / 4)
+};
+__global__ void qkv_prologue_kernel(QkvPrologueArgs a);
+
 // Unfused forward: the three operators whose composition the fused kernel
 // reproduces byte for byte.  Intermediates are dense per (b, h) row-major
 // over the query rows, with Kp = 64 * nt_max key slots per row: slot 64*t + j

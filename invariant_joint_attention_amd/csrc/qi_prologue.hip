@@ -19,6 +19,7 @@
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_rope.h"
+#include "qi_vtiles.h"
 
 namespace qi {
 
@@ -53,9 +54,10 @@ __device__ __forceinline__ float row_rinv(const float* xf, float eps) {
   return 1.0f / sqrtf(ms + eps);
 }
 
-__global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(PrologueArgs a) {
+// Tokens 4 blk .. 4 blk + 3 of the launch, one per wave.
+__device__ __forceinline__ void prologue_body(const PrologueArgs& a, int64_t blk) {
   const int lane = threadIdx.x & 63;
-  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tok = blk * 4 + (threadIdx.x >> 6);
   if (tok >= (int64_t)a.B * a.S) return;  // wave-uniform; no block barrier follows
   const int b = (int)(tok / a.S), s = (int)(tok - (int64_t)b * a.S);
 
@@ -108,6 +110,25 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(PrologueArgs a) {
         *(f32x4*)(dst + 4) = f32x4{yo[4], yo[5], yo[6], yo[7]};
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(PrologueArgs a) { prologue_body(a, blockIdx.x); }
+
+// The Q and K prologues and the V tile conversion of a forward in one launch:
+// blocks [0, nblk) take Q's tokens, [nblk, 2 nblk) K's, and the rest one V
+// key tile each, (t, h, b) in row-major order.  Each part runs exactly the
+// arithmetic of its own kernel, so every output byte is the same.
+__global__ __launch_bounds__(256) void qkv_prologue_kernel(QkvPrologueArgs a) {
+  const int64_t bx = blockIdx.x;
+  if (bx < a.nblk) {
+    prologue_body(a.q, bx);
+  } else if (bx < 2 * a.nblk) {
+    prologue_body(a.k, bx - a.nblk);
+  } else {
+    const int64_t r = bx - 2 * a.nblk;
+    const int64_t th = r / a.v.nt_max;
+    v_tile_body(a.v, (int)(r - th * a.v.nt_max), (int)(th % a.v.H), (int)(th / a.v.H));
   }
 }
 

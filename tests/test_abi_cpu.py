@@ -338,3 +338,43 @@ def test_projection_validation():
     assert out(streams=0) == code("QI_E_INVALID")
     assert out(y=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")
     assert out(bias=None) == code("QI_E_INVALID")
+
+
+def test_qkv_prologue_and_pretiled_forward_validation():
+    g = geom()
+    L = qi.lib()
+    vt_bytes = L.qi_joint_attn_fwd_workspace(g.ptr())
+    qr, kr, v = (fake_bshd(region(i), g.B, g.S, g.H) for i in range(3))
+    q, k = fake_bshd(region(3), g.B, g.S, g.H), fake_bshd(region(4), g.B, g.S, g.H)
+    gq, gk, vt = region(5), region(6), region(7)
+
+    def pro(**kw):
+        a = dict(qr=qr, kr=kr, v=v, gq=gq, gk=gk, q=q, k=k, vt=vt, n=vt_bytes)
+        a.update(kw)
+        return L.qi_qkv_prologue(g.ptr(), a["qr"], a["kr"], a["v"], a["gq"], a["gk"], a["q"], a["k"], a["vt"],
+                                 a["n"], None)
+
+    assert pro() == code("QI_E_UNSUPPORTED")  # valid: stops at the device gate
+    assert pro(vt=0) == code("QI_E_WORKSPACE")
+    assert pro(n=vt_bytes - 1) == code("QI_E_WORKSPACE")
+    assert pro(vt=vt + 16) == code("QI_E_ALIGN")
+    assert pro(gk=None) == code("QI_E_INVALID")
+    assert pro(k=q) == code("QI_E_ALIAS")                      # two outputs on one buffer
+    assert pro(vt=region(2)) == code("QI_E_ALIAS")             # tiles over the V input
+    assert pro(q=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")  # q' over q_raw
+
+    o = fake_bshd(region(8), g.B, g.S, g.H)
+    lse = region(9)
+
+    def fwd(**kw):
+        a = dict(q=q, k=k, vt=vt, n=vt_bytes, o=o, lse=lse, of=None)
+        a.update(kw)
+        return L.qi_joint_attn_fwd_vtiles(g.ptr(), a["q"], a["k"], a["vt"], a["n"], a["o"], a["lse"], a["of"], None)
+
+    assert fwd() == code("QI_E_UNSUPPORTED")
+    assert fwd(vt=0) == code("QI_E_WORKSPACE")
+    assert fwd(n=vt_bytes - 1) == code("QI_E_WORKSPACE")
+    assert fwd(vt=vt + 16) == code("QI_E_ALIGN")
+    assert fwd(o=fake_bshd(vt, g.B, g.S, g.H)) == code("QI_E_ALIAS")  # output over the tiles
+    assert fwd(vt=region(0)) != code("QI_E_ALIAS")                     # the tiles are read only
+    assert fwd(lse=region(9) + 2) == code("QI_E_ALIGN")

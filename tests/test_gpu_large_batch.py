@@ -99,3 +99,19 @@ def test_blocks_unfused_projections_rows_equal_alone(case):
         assert _same(om1, om[b:b + 1]) and _same(lm1, lm[b:b + 1]), f"merged row {b}"
         for t1, t in ((pq1, pq), (pk1, pk), (pv1, pv), (y1, y)):
             assert _same(t1, t[b:b + 1]), f"projection row {b}"
+
+
+def test_qkv_prologue_path_equals_separate_calls(case):
+    """The one-launch Q/K/V prologue and the forward over its tiles, at a
+    batch of two launches: the same bytes as the separate prologues and
+    the forward call."""
+    wl, g, geo = case
+    print("large batch: fused prologue path", flush=True)
+    q = qi.qknorm_rope(g["q"], g["g_q"], geo)
+    k = qi.qknorm_rope(g["k"], g["g_k"], geo)
+    o, lse = qi.joint_attn_fwd(q, k, g["v"], geo)
+    qf, kf, vt = qi.qkv_prologue(g["q"], g["k"], g["v"], g["g_q"], g["g_k"], geo)
+    of_, lf = qi.joint_attn_fwd_vtiles(qf, kf, vt, geo)
+    torch.cuda.synchronize()
+    assert _same(qf, q) and _same(kf, k)
+    assert _same(of_, o) and _same(lf, lse)
