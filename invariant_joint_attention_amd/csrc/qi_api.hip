@@ -431,36 +431,43 @@ int launch_prologue(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd y, f
   return launched("qknorm_rope_fwd_kernel");
 }
 
-int launch_prologue_bwd(const qi_geom* g, qi_bshd x, const float* gain, qi_bshd dx, float* partials,
-                        float* dg_ps, float* dg, const BwdLayout& Lw, hipStream_t st) {
-  PrologueBwdArgs a;
-  a.x = view_of<const uint16_t>(x, 0);
-  a.dx = view_of<float>(dx, 0);
-  a.gain = gain;
-  a.partials = partials;
-  a.gain_streams = g->gain_streams;
-  a.B = g->B;
-  a.S = (int)seq_len(g);
-  a.H = g->H;
-  a.T_txt = g->T_txt;
-  a.gh = g->grid_h;
-  a.gw = g->grid_w;
-  a.n_txt_chunks = Lw.n_txt_chunks;
-  a.n_chunks = Lw.n_chunks;
-  a.theta = g->rope_theta;
-  a.eps = g->rms_eps;
-  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(Lw.n_chunks, g->B), dim3(256), 0, st, a);
+// The prologue backward of both gradients (t = 0: q, 1: k) in one launch,
+// then both gain folds in one launch.
+int launch_prologue_bwd(const qi_geom* g, const qi_bshd x[2], const float* const gain[2], const qi_bshd dx[2],
+                        float* const partials[2], float* const dg_ps[2], float* const dg[2], const BwdLayout& Lw,
+                        hipStream_t st) {
+  PrologueBwdPair pp;
+  DgainFoldPair fp;
+  for (int t = 0; t < 2; ++t) {
+    PrologueBwdArgs& a = pp.t[t];
+    a.x = view_of<const uint16_t>(x[t], 0);
+    a.dx = view_of<float>(dx[t], 0);
+    a.gain = gain[t];
+    a.partials = partials[t];
+    a.gain_streams = g->gain_streams;
+    a.B = g->B;
+    a.S = (int)seq_len(g);
+    a.H = g->H;
+    a.T_txt = g->T_txt;
+    a.gh = g->grid_h;
+    a.gw = g->grid_w;
+    a.n_txt_chunks = Lw.n_txt_chunks;
+    a.n_chunks = Lw.n_chunks;
+    a.theta = g->rope_theta;
+    a.eps = g->rms_eps;
+    DgainFoldArgs& f = fp.t[t];
+    f.partials = partials[t];
+    f.dg_ps = dg_ps[t];
+    f.dg = dg[t];
+    f.B = g->B;
+    f.gain_streams = g->gain_streams;
+    f.n_txt_chunks = Lw.n_txt_chunks;
+    f.n_chunks = Lw.n_chunks;
+  }
+  hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(Lw.n_chunks, g->B, 2), dim3(256), 0, st, pp);
   int rc = launched("qknorm_rope_bwd_kernel");
   if (rc) return rc;
-  DgainFoldArgs f;
-  f.partials = partials;
-  f.dg_ps = dg_ps;
-  f.dg = dg;
-  f.B = g->B;
-  f.gain_streams = g->gain_streams;
-  f.n_txt_chunks = Lw.n_txt_chunks;
-  f.n_chunks = Lw.n_chunks;
-  hipLaunchKernelGGL(dgain_fold_kernel, dim3(g->gain_streams), dim3(kHeadDim), 0, st, f);
+  hipLaunchKernelGGL(dgain_fold_kernel, dim3(g->gain_streams, 2), dim3(kHeadDim), 0, st, fp);
   return launched("dgain_fold_kernel");
 }
 
@@ -963,9 +970,12 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     hipLaunchKernelGGL(attn_bwd_dv_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
     if ((rc = launched("attn_bwd_dv_kernel"))) return rc;
   }
-  if ((rc = launch_prologue_bwd(geom, q_raw, gain_q, dq, (float*)(ws + Lw.pq), dgain_q_ps, dgain_q, Lw, stream)))
-    return rc;
-  return launch_prologue_bwd(geom, k_raw, gain_k, dk, (float*)(ws + Lw.pk), dgain_k_ps, dgain_k, Lw, stream);
+  const qi_bshd xs[2] = {q_raw, k_raw}, dxs[2] = {dq, dk};
+  const float* const gains[2] = {gain_q, gain_k};
+  float* const parts[2] = {(float*)(ws + Lw.pq), (float*)(ws + Lw.pk)};
+  float* const dg_ps[2] = {dgain_q_ps, dgain_k_ps};
+  float* const dg[2] = {dgain_q, dgain_k};
+  return launch_prologue_bwd(geom, xs, gains, dxs, parts, dg_ps, dg, Lw, stream);
 }
 
 const char* qi_trace(void) {

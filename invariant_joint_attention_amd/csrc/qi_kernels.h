@@ -100,8 +100,16 @@ struct BwdArgs {
 };
 
 __global__ void qknorm_rope_fwd_kernel(PrologueArgs a);
-__global__ void qknorm_rope_bwd_kernel(PrologueBwdArgs a);
-__global__ void dgain_fold_kernel(DgainFoldArgs a);
+// The Q and K gradients go through one launch each: grid z (prologue
+// backward) or y (fold) selects the tensor.
+struct PrologueBwdPair {
+  PrologueBwdArgs t[2];
+};
+struct DgainFoldPair {
+  DgainFoldArgs t[2];
+};
+__global__ void qknorm_rope_bwd_kernel(PrologueBwdPair p);
+__global__ void dgain_fold_kernel(DgainFoldPair p);
 __global__ void attn_fwd_kernel(FwdArgs a);
 __global__ void attn_fwd_partial_kernel(FwdArgs a);
 __global__ void attn_merge_kernel(MergeArgs a);

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(QkvPrologueArgs a) {
 // chunk in order; inside a wave each lane accumulates its 8 channels over
 // its rows, the four lane groups are combined by an xor tree (16, 32), and
 // the four waves are added in order 0,1,2,3.
-__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(PrologueBwdArgs a) {
+__global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(PrologueBwdPair p) {
+  const PrologueBwdArgs a = blockIdx.z ? p.t[1] : p.t[0];  // Q's or K's gradient (uniform)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int chunk = blockIdx.x;  // 0 .. n_txt_chunks + n_img_chunks - 1
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(PrologueBwdArgs a)
 // Fold the chunk partials of each sample and gain set in ascending chunk
 // order, then (one thread per channel and set) the per-sample results in
 // ascending b.  Grid: (gain_streams), block: 128 x B-independent loop.
-__global__ __launch_bounds__(128) void dgain_fold_kernel(DgainFoldArgs a) {
+__global__ __launch_bounds__(128) void dgain_fold_kernel(DgainFoldPair p) {
+  const DgainFoldArgs a = blockIdx.y ? p.t[1] : p.t[0];  // Q's or K's gain (uniform)
   const int set = blockIdx.x, cc = threadIdx.x;
   int k0, k1;
   if (a.gain_streams == 2) {
