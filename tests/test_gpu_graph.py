@@ -17,13 +17,14 @@ def _same(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
+@pytest.mark.parametrize("fused_prologue", [False, True], ids=["separate_prologue", "qkv_prologue"])
 @pytest.mark.parametrize("name", ["ragged", "1024sq_bwd"])
-def test_graph_replay_matches_eager(name):
+def test_graph_replay_matches_eager(name, fused_prologue):
     if name == "ragged":
         wl = workloads.custom("ragged", 3, 2, 130, (0, 67, 130), 9, 11, 500, backward=True)
     else:
         wl = workloads.WORKLOADS[name]
-    print(f"graph replay: {wl.name}", flush=True)
+    print(f"graph replay: {wl.name} fused_prologue={fused_prologue}", flush=True)
     inp = workloads.make_inputs(wl)
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     geo = qi.Geometry(B=wl.B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w, txt_len=list(wl.txt_len))
@@ -42,9 +43,14 @@ def test_graph_replay_matches_eager(name):
                     dv=torch.empty(shp, dtype=torch.float32, device=DEV))
 
     def step(b):
-        qi.qknorm_rope(g["q"], g["g_q"], geo, out=b["qp"])
-        qi.qknorm_rope(g["k"], g["g_k"], geo, out=b["kp"])
-        qi.joint_attn_fwd(b["qp"], b["kp"], g["v"], geo, out=b["o"], lse=b["lse"], out_f32=b["of"], workspace=b["fws"])
+        if fused_prologue:
+            qi.qkv_prologue(g["q"], g["k"], g["v"], g["g_q"], g["g_k"], geo, q=b["qp"], k=b["kp"], v_tiles=b["fws"])
+            qi.joint_attn_fwd_vtiles(b["qp"], b["kp"], b["fws"], geo, out=b["o"], lse=b["lse"], out_f32=b["of"])
+        else:
+            qi.qknorm_rope(g["q"], g["g_q"], geo, out=b["qp"])
+            qi.qknorm_rope(g["k"], g["g_k"], geo, out=b["kp"])
+            qi.joint_attn_fwd(b["qp"], b["kp"], g["v"], geo, out=b["o"], lse=b["lse"], out_f32=b["of"],
+                              workspace=b["fws"])
         r = qi.joint_attn_bwd(g["q"], g["k"], b["qp"], b["kp"], g["v"], b["of"], b["lse"], g["dO"], g["g_q"], g["g_k"],
                               geo, workspace=b["bws"], dq=b["dq"], dk=b["dk"], dv=b["dv"])
         return r
