@@ -378,3 +378,20 @@ def test_qkv_prologue_and_pretiled_forward_validation():
     assert fwd(o=fake_bshd(vt, g.B, g.S, g.H)) == code("QI_E_ALIAS")  # output over the tiles
     assert fwd(vt=region(0)) != code("QI_E_ALIAS")                     # the tiles are read only
     assert fwd(lse=region(9) + 2) == code("QI_E_ALIGN")
+
+
+def test_backward_head_limit_and_workspace_parts():
+    """The backward's workspace holds at least D (FP32 per row) and the FP16
+    copy of dO; a head count beyond the 65,535 its launches address is
+    refused before the device gate."""
+    L = qi.lib()
+    g = geom()
+    ws = L.qi_joint_attn_bwd_workspace(g.ptr())
+    assert ws >= g.B * g.H * g.S * 4 + g.B * g.S * g.H * 128 * 2
+    g = geom(H=65536)
+    ws = L.qi_joint_attn_bwd_workspace(g.ptr())
+    views = [fake_bshd(region(i), g.B, g.S, g.H) for i in range(6)]
+    grads = [fake_bshd(region(10 + i), g.B, g.S, g.H) for i in range(3)]
+    rc = L.qi_joint_attn_bwd(g.ptr(), *views, region(6), fake_bshd(region(7), g.B, g.S, g.H), region(8), region(9),
+                             *grads, region(14), region(15), None, None, region(20), ws, None)
+    assert rc == code("QI_E_UNSUPPORTED") and "65535" in qi.last_error(), qi.last_error()
