@@ -358,40 +358,48 @@ void oracle_attn_softmax_rows(int n, int S, int T_txt, int L, const real* s, rea
     softmax_row(S, all_keys(S, T_txt, L), s + (int64_t)i * S, p + (int64_t)i * S, &lse[i]);
 }
 
-/* The A.V step of the online softmax [Kernel list, row joint_attn_av_gemm;
+/* The A.V operator of the online softmax [Kernel list, row joint_attn_av_gemm;
  * row joint_attn_softmax: the softmax runs over the key sequence in a fixed
  * tiling].  Keys of a row with text length L are split into logical tiles of
  * 64: ceil(L/64) tiles of text keys 64t .. (up to L), then the image keys
- * T_txt + 64u .. (up to S).  With P[i][t][j] the weight of key j of tile t
- * and alpha[i][t] the factor that rescales what was accumulated before tile
- * t:
- *   acc <- alpha_t * acc + sum_j P[t][j] v_key(t,j)   for t = 0, 1, ...
- *   o = acc / l.
- * P [n][nt][64] and alpha [n][nt] for nt tile slots (slots past the row's
- * tiles, and past a tile's keys, are ignored); l [n]; v [S][128]. */
+ * T_txt + 64u .. (up to S).  P[i][t][j] is the weight of key j of tile t and
+ * alpha[i][t] the factor by which the operator rescales what the tiles
+ * before t contributed, so tile t's contribution carries the product of the
+ * factors of every later tile:
+ *   o_i = ( sum_t w_t sum_j P[i][t][j] v_key(t,j) ) / l_i,
+ *   w_t = prod_{u > t} alpha[i][u]   (w of the row's last tile = 1),
+ * both sums in ascending t, j.  P [n][nt][64] and alpha [n][nt] for nt tile
+ * slots (slots past the row's tiles, and past a tile's keys, are ignored);
+ * l [n]; v [S][128]. */
 void oracle_attn_av_rows(int n, int S, int T_txt, int L, int nt, const real* P,
                          const real* alpha, const real* l, const real* v, real* o) {
   const int T_img = S - T_txt;
   const int ntxt = (L + 63) / 64, nimg = (T_img + 63) / 64;
+  const int ntile = ntxt + nimg < nt ? ntxt + nimg : nt;
 #pragma omp parallel for schedule(static)
   for (int i = 0; i < n; ++i) {
+    real* w = (real*)malloc(sizeof(real) * (size_t)(ntile > 0 ? ntile : 1));
+    for (int t = 0; t < ntile; ++t) {
+      real prod = 1;
+      for (int u = t + 1; u < ntile; ++u) prod = prod * alpha[(int64_t)i * nt + u];
+      w[t] = prod;
+    }
     real acc[HD];
     for (int c = 0; c < HD; ++c) acc[c] = 0;
-    for (int t = 0; t < ntxt + nimg && t < nt; ++t) {
-      const real a = alpha[(int64_t)i * nt + t];
-      for (int c = 0; c < HD; ++c) acc[c] = a * acc[c];
+    for (int t = 0; t < ntile; ++t) {
       const int first = t < ntxt ? 64 * t : T_txt + 64 * (t - ntxt);
       const int end = t < ntxt ? L : S;
       for (int j = 0; j < 64 && first + j < end; ++j) {
-        const real pj = P[((int64_t)i * nt + t) * 64 + j];
+        const real wp = w[t] * P[((int64_t)i * nt + t) * 64 + j];
         const real* vj = v + (int64_t)(first + j) * HD;
         for (int c = 0; c < HD; ++c) {
-          real pr = pj * vj[c];
+          real pr = wp * vj[c];
           acc[c] = acc[c] + pr;
         }
       }
     }
     for (int c = 0; c < HD; ++c) o[(int64_t)i * HD + c] = acc[c] / l[i];
+    free(w);
   }
 }
 
@@ -443,15 +451,17 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
         }
         ds[j] = p[j] * (dp - Di);
       }
-      for (int c = 0; c < HD; ++c) {
-        real acc = 0;
-        for (int j = 0; j < S; ++j) {
-          if (!key_valid(j, ks)) continue;
+      /* dq_ic = sum_j ds_j k_jc, each channel summed in ascending j */
+      real acc[HD];
+      for (int c = 0; c < HD; ++c) acc[c] = 0;
+      for (int j = 0; j < S; ++j) {
+        if (!key_valid(j, ks)) continue;
+        for (int c = 0; c < HD; ++c) {
           real pr = ds[j] * k[(int64_t)j * HD + c];
-          acc = acc + pr;
+          acc[c] = acc[c] + pr;
         }
-        dq[(int64_t)i * HD + c] = acc * sc;
       }
+      for (int c = 0; c < HD; ++c) dq[(int64_t)i * HD + c] = acc[c] * sc;
     }
     free(srow);
   }
@@ -463,16 +473,24 @@ int oracle_attn_bwd_bh(int S, int T_txt, int L, const real* q, const real* k,
       for (int c = 0; c < HD; ++c) { dkj[c] = 0; dvj[c] = 0; }
       continue;
     }
-    for (int c = 0; c < HD; ++c) {
-      real ak = 0, av = 0;
-      for (int i = 0; i < S; ++i) {
-        real pk = dS[(int64_t)i * S + j] * q[(int64_t)i * HD + c];
-        ak = ak + pk;
-        real pv = P[(int64_t)i * S + j] * dO[(int64_t)i * HD + c];
-        av = av + pv;
+    /* dk_jc = sum_i dS_ij q_ic and dv_jc = sum_i P_ij dO_ic, each channel
+     * summed in ascending query order i */
+    real ak[HD], av[HD];
+    for (int c = 0; c < HD; ++c) { ak[c] = 0; av[c] = 0; }
+    for (int i = 0; i < S; ++i) {
+      const real dsij = dS[(int64_t)i * S + j], pij = P[(int64_t)i * S + j];
+      const real* qi = q + (int64_t)i * HD;
+      const real* gi = dO + (int64_t)i * HD;
+      for (int c = 0; c < HD; ++c) {
+        real pk = dsij * qi[c];
+        ak[c] = ak[c] + pk;
+        real pv = pij * gi[c];
+        av[c] = av[c] + pv;
       }
-      dkj[c] = ak * sc;
-      dvj[c] = av;
+    }
+    for (int c = 0; c < HD; ++c) {
+      dkj[c] = ak[c] * sc;
+      dvj[c] = av[c];
     }
   }
   free(P);

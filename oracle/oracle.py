@@ -209,7 +209,8 @@ class Oracle:
         return p, lse
 
     def attn_av_rows(self, P, alpha, l, v, T_txt, L):
-        """The A.V recurrence over logical 64-key tiles: P [n, nt, 64],
+        """The A.V operator over logical 64-key tiles, as its closed form
+        o = sum_t (prod_{u>t} alpha_u) P_t V_t / l: P [n, nt, 64],
         alpha [n, nt], l [n], v [S, 128] -> o [n, 128]."""
         P, alpha, l, v = self._r(P), self._r(alpha), self._r(l), self._r(v)
         n, nt, _ = P.shape
@@ -284,21 +285,6 @@ def forward_path(orc: Oracle, x_q, x_k, v, g_q, g_k, txt_len, T_txt, h, w, heads
     o, lse = orc.attn_fwd(orc.widen(qb), orc.widen(kb), orc.widen(v), txt_len, T_txt, heads=heads)
     ob = orc.cast_bf16(np.nan_to_num(o)) if heads is not None else orc.cast_bf16(o)
     return dict(q_pre=qp, k_pre=kp, q_bf16=qb, k_bf16=kb, o=o, o_bf16=ob, lse=lse)
-
-
-def backward_path(orc: Oracle, x_q, x_k, v, g_q, g_k, dO, txt_len, T_txt, h, w):
-    """Gradients of the whole path for upstream dO (uint16 BF16 bits).
-
-    Attention is differentiated at the oracle's own BF16 q', k' (the values the
-    forward consumes); the prologue backward maps dq', dk' to dq, dk and the
-    gain gradients."""
-    fw = forward_path(orc, x_q, x_k, v, g_q, g_k, txt_len, T_txt, h, w)
-    dqp, dkp, dv = orc.attn_bwd(orc.widen(fw["q_bf16"]), orc.widen(fw["k_bf16"]), orc.widen(v),
-                                orc.widen(dO), txt_len, T_txt)
-    dq, dgq = orc.qknorm_rope_bwd(orc.widen(x_q), g_q, dqp, T_txt, h, w)
-    dk, dgk = orc.qknorm_rope_bwd(orc.widen(x_k), g_k, dkp, T_txt, h, w)
-    return dict(fw=fw, dq_pre=dqp, dk_pre=dkp, dv=dv, dq=dq, dk=dk,
-                dgq_ps=dgq, dgk_ps=dgk, dgq=fold_batch(dgq), dgk=fold_batch(dgk))
 
 
 def qkv_path(orc: Oracle, x, W, bias, g_q, g_k, T_txt, h, w):

@@ -17,7 +17,7 @@ import torch.nn.functional as F
 from scipy.special import logsumexp
 
 import workloads
-from oracle import Oracle, fold_batch, forward_path
+from oracle import Oracle, fold_batch, forward_path, qkv_path
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 HD = 128
@@ -488,16 +488,72 @@ def test_backward_attention_identities(o32):
             assert np.abs(dv[b, :, hh] - ref).max() < 1e-5
 
 
-def test_forward_path_composes(o32):
-    """forward_path = prologue, single BF16 cast, attention on the cast values."""
+def test_forward_path_against_library_composition(o32):
+    """forward_path (prologue, one BF16 cast, attention on the cast values)
+    against an independent float64 composition: torch RMSNorm and numpy
+    complex rotation at the hand-written positions, torch's BF16 cast, then
+    torch SDPA with the boolean key mask."""
     wl = workloads.WORKLOADS["tiny"]
     inp = workloads.make_inputs(wl)
     bq, bk, bv = (workloads.bits(inp[n]) for n in ("q", "k", "v"))
-    fw = forward_path(o32, bq, bk, bv, inp["g_q"].numpy(), inp["g_k"].numpy(), inp["txt_len"], wl.T_txt, wl.h, wl.w)
-    assert np.array_equal(fw["q_bf16"], o32.cast_bf16(fw["q_pre"]))
-    o, l = o32.attn_fwd(o32.widen(fw["q_bf16"]), o32.widen(fw["k_bf16"]), o32.widen(bv), inp["txt_len"], wl.T_txt)
-    assert np.array_equal(o, fw["o"]) and np.array_equal(l, fw["lse"])
-    assert fw["o_bf16"].dtype == np.uint16 and fw["o_bf16"].shape == (1, 24, 2, HD)
+    gq, gk = inp["g_q"].numpy(), inp["g_k"].numpy()
+    fw = forward_path(o32, bq, bk, bv, gq, gk, inp["txt_len"], wl.T_txt, wl.h, wl.w)
+    pos = _golden("positions_t8_h4_w4.txt")[:, 1:].astype(np.int32)
+    ref_bits = {}
+    for n, x, g in (("q", inp["q"], gq), ("k", inp["k"], gk)):
+        pre = _torch_prologue(x.double().numpy(), g.astype(np.float64), wl.T_txt, wl.h, wl.w, pos)
+        assert np.abs(fw[f"{n}_pre"] - pre).max() < 2e-5
+        rb = torch.from_numpy(pre).to(torch.bfloat16)
+        ref_bits[n] = rb.view(torch.int16).numpy().view(np.uint16)
+        got = fw[f"{n}_bf16"]
+        # one RNE cast of values that agree to ~1e-6: equal bits except where
+        # a value sits on a rounding boundary (then one BF16 step apart)
+        same = got == ref_bits[n]
+        assert same.mean() > 0.99
+        gv = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).double().numpy()
+        assert np.all(np.abs(gv - rb.double().numpy()) <= 2.0 ** -7 * np.abs(rb.double().numpy()) + 1e-30)
+    widen = lambda u: torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).double().numpy()  # noqa: E731
+    ref_o, ref_l = _sdpa_ref(widen(fw["q_bf16"]), widen(fw["k_bf16"]), widen(bv), inp["txt_len"], wl.T_txt)
+    assert np.abs(fw["o"] - ref_o).max() < 2e-5 and np.abs(fw["lse"] - ref_l).max() < 2e-5
+    ob = torch.from_numpy(fw["o"]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(fw["o_bf16"], ob)
+    assert fw["o_bf16"].shape == (1, 24, 2, HD)
+
+
+def test_qkv_path_against_numpy_composition(o64):
+    """qkv_path against numpy float64: the per-stream projection x W^T + b
+    (text rows with set 0, image rows with set 1), torch's BF16 cast, the
+    packed layout written out index by index (Q channels 0..D-1, K D..2D-1, V
+    2D..3D-1, head h at 128h), then the prologue of the float64 library
+    composition on Q and K."""
+    rng = _rng(23)
+    B, H, T, h, w = 2, 2, 8, 4, 4
+    S, D = T + h * w, H * HD
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    ub = lambda t: t.view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    x = bf(rng.standard_normal((B, S, D)))
+    W = bf(rng.standard_normal((2, 3 * D, D)) / math.sqrt(D))
+    bias = 0.02 * rng.standard_normal((2, 3 * D))
+    gq, gk = 1 + 0.1 * rng.standard_normal((1, HD)), 1 + 0.1 * rng.standard_normal((1, HD))
+    got = qkv_path(o64, ub(x), ub(W), bias, gq, gk, T, h, w)
+    xd, Wd = x.double().numpy(), W.double().numpy()
+    y = np.empty((B, S, 3 * D))
+    y[:, :T] = xd[:, :T] @ Wd[0].T + bias[0]
+    y[:, T:] = xd[:, T:] @ Wd[1].T + bias[1]
+    assert np.abs(got["y"] - y).max() < 1e-12
+    yb = ub(torch.from_numpy(y).to(torch.bfloat16))
+    for i, n in enumerate(("q", "k", "v")):
+        ref = np.empty((B, S, H, HD), dtype=np.uint16)
+        for hh in range(H):
+            for c in range(HD):
+                ref[:, :, hh, c] = yb[:, :, i * D + 128 * hh + c]
+        assert np.array_equal(got[n], ref), n
+    pos = _golden("positions_t8_h4_w4.txt")[:, 1:].astype(np.int32)
+    for n, g in (("q", gq), ("k", gk)):
+        xin = torch.from_numpy(got[n].view(np.int16)).view(torch.bfloat16).double().numpy()
+        pre = _torch_prologue(xin, g[0], T, h, w, pos)
+        rb = ub(torch.from_numpy(pre).to(torch.bfloat16))
+        assert (got[f"{n}_prime"] == rb).mean() > 0.99
 
 
 # ------------------------------------------------- attention, one operator at a time
@@ -571,15 +627,26 @@ def test_operator_av_recurrence(o64, shape):
                                          torch.from_numpy(v)[None], attn_mask=valid[None, None, :].expand(1, S, S))
     assert np.abs(o - ref[0].numpy()).max() < 1e-12
 
+    # (2) arbitrary P, alpha, l: the operator's recurrence acc <- alpha_t acc
+    # + P_t V_t, O = acc / l, run tile by tile in float64 (the route the
+    # operator is specified by; the oracle evaluates the closed form)
     Pr = rng.uniform(0, 2, (n, nt, 64))
     ar = rng.uniform(0.25, 1, (n, nt))
     lr = rng.uniform(1, 64, n)
     o = o64.attn_av_rows(Pr, ar, lr, v, T, L)
-    closed = np.zeros((n, HD))
+    acc = np.zeros((n, HD))
     for t, keys in enumerate(tiles):
-        w_t = np.prod(ar[:, t + 1:len(tiles)], axis=1)
-        closed += w_t[:, None] * (Pr[:, t, :len(keys)] @ v[keys])
-    assert np.abs(o - closed / lr[:, None]).max() < 1e-12
+        acc = ar[:, t:t + 1] * acc + Pr[:, t, :len(keys)] @ v[keys]
+    assert np.abs(o - acc / lr[:, None]).max() < 1e-12
+    # a factor of 0 at tile t erases every tile before it
+    if len(tiles) > 1:
+        az = ar.copy()
+        az[:, 1] = 0.0
+        oz = o64.attn_av_rows(Pr, az, lr, v, T, L)
+        ref = np.zeros((n, HD))
+        for t, keys in enumerate(tiles[1:], start=1):
+            ref = az[:, t:t + 1] * ref + Pr[:, t, :len(keys)] @ v[keys]
+        assert np.abs(oz - ref / lr[:, None]).max() < 1e-12
 
 
 BLOCK_CASES = [  # (T_txt, L, h, w, with_text, img_lo, img_hi)
