@@ -68,6 +68,10 @@ def parse():
                     help="also time the QKV and output projections this many times (0: skip)")
     ap.add_argument("--block-steps", type=int, default=20,
                     help="also time the key-block forward (image keys in blocks of 512) and the merge (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=100,
+                    help="also time the backward of the 1024^2 backward workload this many times (0: skip)")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="also time the attention call this many times with the caches flushed first (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=10,
                     help="also time the unfused forward (scores -> softmax -> A.V) this many times (0: skip)")
     return ap.parse_args()
@@ -92,6 +96,58 @@ def traffic_from_profile(kernel: str, src: str, workload: str):
     return float(m_b.group(1))
 
 
+def host_env(torch):
+    """The machine the numbers come from (GPU, software, host CPU)."""
+    props = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2**30, 1),
+            "rocm_hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu,
+            "host_threads": os.cpu_count()}
+
+
+def sha256_of(*tensors) -> str:
+    """SHA-256 over the raw bytes of the tensors, in order."""
+    import torch
+
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.detach().contiguous().cpu().view(-1).view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
+
+
+class ClockProbe:
+    """Shader clock under a matrix load, sampled by the library's clock probe:
+    one wave per SIMD runs MFMAs for ~30 us and times them against the
+    constant-rate wall clock (both counters read by the same wave)."""
+
+    def __init__(self, qi, torch, groups=1024, iters=512):
+        self.qi, self.iters = qi, iters
+        self.buf = torch.zeros((groups, 3), dtype=torch.int64, device="cuda:0")
+        self.khz = qi.wall_clock_khz(0)
+
+    def sample(self):
+        self.qi.clock_probe(self.buf, self.iters)
+
+    def mhz(self):
+        a = self.buf.cpu().numpy().astype("float64")
+        ticks, wall = a[:, 0], a[:, 1]
+        ok = wall > 0
+        if not ok.any():
+            return None
+        per = ticks[ok] / wall[ok] * self.khz / 1e3
+        return {"mean_mhz": round(float(ticks[ok].sum() / wall[ok].sum() * self.khz / 1e3), 1),
+                "min_mhz": round(float(per.min()), 1), "max_mhz": round(float(per.max()), 1),
+                "waves": int(ok.sum())}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,9 +165,11 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     inp = workloads.make_inputs(wl)
+    in_sha = sha256_of(*(inp[n] for n in ("q", "k", "v", "g_q", "g_k") + (("dO",) if wl.backward else ())))
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     geo = qi.Geometry(B=wl.B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w, txt_len=list(wl.txt_len))
     qi.strict_probe(0)
+    env = host_env(torch)
 
     # preallocated outputs: the timed region launches kernels only
     shp = g["q"].shape
@@ -150,6 +208,22 @@ def main():
     for p in parts:  # eager once (device gate, first-launch costs)
         p()
     torch.cuda.synchronize()
+
+    out = {}
+    # ---- the other measurements of the line come first: each is real work
+    # of the path (not the headline step), and together they run the GPU
+    # long enough for its clock under matrix load to settle before the
+    # headline loop starts
+    aux = {}
+    if args.bwd_steps > 0 and not wl.backward:
+        aux["attn_bwd"] = bench_bwd(qi, torch, np, workloads, args.bwd_steps)
+    if args.block_steps > 0:
+        aux["blocks"] = bench_blocks(qi, torch, np, wl, geo, qp, kp, g["v"], args.block_steps)
+    if args.proj_steps > 0:
+        aux["projections"] = bench_proj(qi, torch, np, workloads, wl, args.proj_steps)
+    if args.unfused_steps > 0:
+        aux["unfused_fwd"] = bench_unfused(qi, torch, np, wl, geo, qp, kp, g["v"], args.unfused_steps)
+
     if not args.graph:
         runs = parts
     else:
@@ -164,33 +238,55 @@ def main():
                 p()
             graphs.append(gr)
         runs = [gr.replay for gr in graphs]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)] for _ in range(args.steps)]
+    # Two events per step, around the attention call (the prologue of the
+    # next step follows the second one): every event record costs the stream
+    # a few microseconds, so the step carries no more of them than the
+    # attention timing needs.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    j_fwd = names.index("fwd")
+    clock = ClockProbe(qi, torch)
 
     def step(e=None):
-        if e is not None:
-            e[0].record()
         for i, r in enumerate(runs):
+            if e is not None and i == j_fwd:
+                e[0].record()
             r()
-            if e is not None:
-                e[i + 1].record()
+            if e is not None and i == j_fwd:
+                e[1].record()
 
     for _ in range(args.warmup):
         step()
+    clock.sample()
     torch.cuda.synchronize()
+    clock_before = clock.mhz()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.sample()
+    torch.cuda.synchronize()
+    clock_after = clock.mhz()
     ms_step = wall * 1e3 / args.steps
+    out_sha = sha256_of(o, lse)
 
-    def avg_ms(name):
-        if name not in names:
-            return 0.0
-        j = names.index(name)
-        return float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+    fwd_t = [e[0].elapsed_time(e[1]) for e in ev]
+    fwd_ms = float(np.mean(fwd_t))
 
-    pro_ms, fwd_ms, bwd_ms = avg_ms("pro"), avg_ms("fwd"), avg_ms("bwd")
+    def part_ms(fn, n=10):
+        """A part of the step timed on its own after the headline loop."""
+        es = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            es.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in es]))
+
+    pro_ms = part_ms(runs[names.index("pro")])
+    bwd_ms = part_ms(runs[names.index("bwd")]) if wl.backward else 0.0
     fwd_flops = wl.fwd_flops()
     value = fwd_flops / (ms_step * 1e-3) / 1e12
     attn_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -212,7 +308,27 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "flops_per_launch": fwd_flops, "avg_launch_ms": round(fwd_ms, 4)}
 
-    out = {
+    # the attention call again with the caches flushed before each launch
+    # (inputs read from HBM, not from the 256 MB last-level cache)
+    flushed = None
+    if args.flush_steps > 0:
+        junk = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+        fe = []
+        for _ in range(args.flush_steps):
+            junk.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fwd()
+            e1.record()
+            fe.append((e0, e1))
+        torch.cuda.synchronize()
+        ft = [a.elapsed_time(b) for a, b in fe]
+        flushed = {"steps": args.flush_steps, "median_ms": round(float(np.median(ft)), 4),
+                   "min_ms": round(float(np.min(ft)), 4),
+                   "tflops_median": round(fwd_flops / (float(np.median(ft)) * 1e-3) / 1e12, 1)}
+        del junk
+
+    out.update({
         "metric": "joint-attn fwd TFLOP/s and % BF16 MFMA peak at 1024^2 (S=4096+256), 24x128",
         "value": round(value, 2),
         "unit": "TFLOP/s",
@@ -223,20 +339,34 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp16",
+        "dtype_detail": "QK^T on BF16 MFMA (v_mfma_f32_32x32x16_bf16); P.V on FP16 MFMA "
+                        "(v_mfma_f32_32x32x16_f16, FP16 P and FP16 V*2^-8); FP32 accumulation; "
+                        "prologue FP32 with one BF16 output cast",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.note}", "B": wl.B, "heads": wl.H, "head_dim": 128,
                    "T_txt": wl.T_txt, "txt_len": list(wl.txt_len), "grid": [wl.h, wl.w], "S": wl.S,
                    "backward": wl.backward},
+        "env": env,
+        "sha256": {"inputs": in_sha, "outputs_o_lse": out_sha},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "attn_fwd": {"ms": round(fwd_ms, 4), "tflops": round(attn_tflops, 2),
-                     "pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2)},
+        "attn_fwd": {"ms": round(fwd_ms, 4), "median_ms": round(float(np.median(fwd_t)), 4),
+                     "min_ms": round(float(np.min(fwd_t)), 4), "max_ms": round(float(np.max(fwd_t)), 4),
+                     "tflops": round(attn_tflops, 2),
+                     "pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+                     "pct_peak_median": round(100 * fwd_flops / (float(np.median(fwd_t)) * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 2),
+                     "cache_flushed": flushed},
+        "shader_clock": {"before_timed_steps": clock_before, "after_timed_steps": clock_after,
+                         "how": "per wave: s_memtime ticks / s_memrealtime ticks x wall-clock rate, one wave "
+                                "per SIMD running BF16 MFMAs for ~30 us, sampled just before and just after "
+                                "the timed steps"},
         "prologue": {"calls": "qi_qknorm_rope x 2" if args.separate_prologue else "qi_qkv_prologue (Q, K, V tiles)",
-                     "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                     "timed": "10 calls on their own after the timed steps", "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "launch": "hip_graph_replay" if args.graph else "eager",
-    }
+    })
     if wl.backward:
         bflops = wl.bwd_flops()
         out["attn_bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
@@ -244,15 +374,12 @@ def main():
         # the whole step (prologues, forward, backward) against forward + backward FLOPs
         out["fwd_bwd_step"] = {"ms": round(ms_step, 4), "flops": fwd_flops + bflops,
                                "tflops": round((fwd_flops + bflops) / (ms_step * 1e-3) / 1e12, 2)}
-
-    if args.block_steps > 0:
-        out["blocks"] = bench_blocks(qi, torch, np, wl, geo, qp, kp, g["v"], args.block_steps, fwd_ms)
-
-    if args.proj_steps > 0:
-        out["projections"] = bench_proj(qi, torch, np, workloads, wl, args.proj_steps)
-
-    if args.unfused_steps > 0:
-        out["unfused_fwd"] = bench_unfused(qi, torch, np, wl, geo, qp, kp, g["v"], args.unfused_steps, fwd_ms)
+    for k_, v_ in aux.items():
+        if isinstance(v_, dict) and "ms" in v_ and k_ in ("blocks", "unfused_fwd"):
+            v_["vs_fused"] = round(v_["ms"] / fwd_ms, 3)
+        out[k_] = v_
+    out["order"] = ("the other measurements (" + ", ".join(aux) + ") ran before the headline loop; "
+                    "then warmup and the timed steps") if aux else "warmup, then the timed steps"
 
     # ---------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
@@ -261,7 +388,54 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, fused_ms, block=512):
+def bench_bwd(qi, torch, np, workloads, steps):
+    """The deterministic backward of the 1024^2 backward workload (same
+    shapes as the forward workload, its own seed, plus dO): the prologues and
+    the forward (keeping the FP32 O) once, then `steps` backward calls, each
+    timed with HIP events on the launch stream against the dense BF16 MFMA
+    peak on the algorithmic count 10 * D * H * S * K."""
+    dev = "cuda:0"
+    wl = workloads.WORKLOADS["1024sq_bwd"]
+    inp = workloads.make_inputs(wl)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    geo = qi.Geometry(B=wl.B, H=wl.H, T_txt=wl.T_txt, grid_h=wl.h, grid_w=wl.w, txt_len=list(wl.txt_len))
+    q = qi.qknorm_rope(g["q"], g["g_q"], geo)
+    k = qi.qknorm_rope(g["k"], g["g_k"], geo)
+    of = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    o, lse = qi.joint_attn_fwd(q, k, g["v"], geo, out_f32=of)
+    ws = torch.empty(qi.bwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
+    grads = {n: torch.empty(q.shape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
+    dgq = torch.empty((wl.B, 1, 128), dtype=torch.float32, device=dev)
+    dgk = torch.empty_like(dgq)
+    dgq_f, dgk_f = torch.empty((1, 128), dtype=torch.float32, device=dev), torch.empty((1, 128), dtype=torch.float32,
+                                                                                          device=dev)
+
+    def run():
+        qi.joint_attn_bwd(g["q"], g["k"], q, k, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo, workspace=ws,
+                          dgain_q_ps=dgq, dgain_k_ps=dgk, dgain_q=dgq_f, dgain_k=dgk_f, **grads)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    flops = wl.bwd_flops()
+    ms = float(np.mean(t))
+    return {"workload": f"{wl.name}: {wl.note}", "steps": steps, "calls": "qi_joint_attn_bwd",
+            "ms": round(ms, 4), "median_ms": round(float(np.median(t)), 4), "min_ms": round(float(np.min(t)), 4),
+            "algorithmic_flops": flops, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+            "sha256_outputs": sha256_of(grads["dq"], grads["dk"], grads["dv"], dgq, dgk)}
+
+
+def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
     """The key-block forward as a sequence-parallel split would run it: the
     image keys in blocks of `block` keys (the text keys in block 0), one
     partial call per block, then the fixed-order merge; each timed with HIP
@@ -311,7 +485,7 @@ def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, fused_ms, block=512):
                          "frac": round(flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"},
             "merge": {"ms": round(m_ms, 4), "bytes": m_bytes, "gbps": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
                       "frac": round(m_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bound": "hbm"},
-            "ms": round(p_ms + m_ms, 4), "vs_fused": round((p_ms + m_ms) / fused_ms, 3)}
+            "ms": round(p_ms + m_ms, 4)}
 
 
 def bench_proj(qi, torch, np, workloads, wl, steps):
@@ -361,7 +535,7 @@ def bench_proj(qi, torch, np, workloads, wl, steps):
     return res
 
 
-def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps, fused_ms):
+def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps):
     """The three unfused operators on the same inputs, each timed with HIP
     events on the launch stream, against the HBM roofline of the arrays each
     one reads and writes (scores FP32 and P FP16 over all key slots, the tile
@@ -415,7 +589,6 @@ def bench_unfused(qi, torch, np, wl, geo, q, k, v, steps, fused_ms):
         gbps = nb / (ms * 1e-3) / 1e9
         res[n] = {"ms": round(ms, 4), "bytes": nb, "gbps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     res["ms"] = round(total, 4)
-    res["vs_fused"] = round(total / fused_ms, 3)
     return res
 
 

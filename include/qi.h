@@ -383,6 +383,24 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
                       float* dgain_k, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * Measurement support (not part of the attention path).
+ *
+ * qi_clock_probe -- enqueue one launch of n_groups single-wave workgroups;
+ * each reads the shader clock counter (s_memtime) and the constant-rate
+ * wall clock (s_memrealtime), runs `iters` rounds of four BF16 MFMAs, reads
+ * both again and writes out[3i] = shader-clock ticks, out[3i+1] = wall-clock
+ * ticks elapsed in between (out[3i+2] keeps the MFMA result alive).
+ * (ticks / wall ticks) * qi_wall_clock_khz() is the wave's average shader
+ * clock in kHz while the chip carries a matrix load.
+ *   out      device uint64 [n_groups][3], 8-byte aligned; 1 <= n_groups <= 65536,
+ *            1 <= iters <= 2^20.
+ * qi_wall_clock_khz -- rate of the wall clock of `device` in kHz (0 and
+ * QI_E_HIP in qi_last_error() if it cannot be queried).
+ */
+int qi_clock_probe(uint64_t* out, int32_t n_groups, int32_t iters, hipStream_t stream);
+int64_t qi_wall_clock_khz(int device);
+
 /* Message for the calling thread's last nonzero status ("" if none). */
 const char* qi_last_error(void);
 

@@ -27,7 +27,8 @@ SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd",
            "qi_joint_attn_merge", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
            "qi_joint_attn_key_slots",
            "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
-           "qi_joint_attn_bwd", "qi_last_error", "qi_strict_probe", "qi_trace")
+           "qi_joint_attn_bwd", "qi_clock_probe", "qi_wall_clock_khz", "qi_last_error", "qi_strict_probe",
+           "qi_trace")
 
 
 class QiError(RuntimeError):
@@ -85,13 +86,16 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_bwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_bwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, QiBshd, P, QiBshd, P, P,
                                         QiBshd, QiBshd, QiBshd, P, P, P, P, P, ctypes.c_size_t, S]
+        L.qi_clock_probe.argtypes = [P, ctypes.c_int32, ctypes.c_int32, S]
+        L.qi_wall_clock_khz.argtypes = [ctypes.c_int]
+        L.qi_wall_clock_khz.restype = ctypes.c_int64
         L.qi_last_error.restype = ctypes.c_char_p
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
         for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
                      "qi_qkv_proj", "qi_attn_out_proj",
                      "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
-                     "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_strict_probe"):
+                     "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_clock_probe", "qi_strict_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -307,7 +311,7 @@ def bwd_workspace_bytes(geom: Geometry) -> int:
 
 
 def joint_attn_bwd(q_raw, k_raw, q, k, v, o_f32, lse, d_o, gain_q, gain_k, geom: Geometry, workspace=None,
-                   dq=None, dk=None, dv=None):
+                   dq=None, dk=None, dv=None, dgain_q_ps=None, dgain_k_ps=None, dgain_q=None, dgain_k=None):
     """Gradients of the whole path (o_f32: the forward's FP32 pre-cast O).
     Returns a dict with dq, dk, dv (FP32
     [B,S,H,128], w.r.t. the raw prologue inputs and V), dgain_q_ps /
@@ -319,10 +323,11 @@ def joint_attn_bwd(q_raw, k_raw, q, k, v, o_f32, lse, d_o, gain_q, gain_k, geom:
     dk = torch.empty(shp, dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty(shp, dtype=torch.float32, device=dev) if dv is None else dv
     ns = geom.gain_streams
-    dgq_ps = torch.empty((geom.B, ns, HEAD_DIM), dtype=torch.float32, device=dev)
-    dgk_ps = torch.empty((geom.B, ns, HEAD_DIM), dtype=torch.float32, device=dev)
-    dgq = torch.empty((ns, HEAD_DIM), dtype=torch.float32, device=dev)
-    dgk = torch.empty((ns, HEAD_DIM), dtype=torch.float32, device=dev)
+    def buf(t, shape):
+        return torch.empty(shape, dtype=torch.float32, device=dev) if t is None else t
+
+    dgq_ps, dgk_ps = buf(dgain_q_ps, (geom.B, ns, HEAD_DIM)), buf(dgain_k_ps, (geom.B, ns, HEAD_DIM))
+    dgq, dgk = buf(dgain_q, (ns, HEAD_DIM)), buf(dgain_k, (ns, HEAD_DIM))
     nbytes = bwd_workspace_bytes(geom)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -354,3 +359,18 @@ def trace() -> str:
 
 def last_error() -> str:
     return lib().qi_last_error().decode()
+
+
+def clock_probe(out: torch.Tensor, iters: int = 512) -> None:
+    """Enqueue the shader-clock probe into ``out`` (int64 [n, 3] on the
+    device): per single-wave workgroup the shader-clock and wall-clock ticks
+    over `iters` rounds of four BF16 MFMAs."""
+    assert out.dtype == torch.int64 and out.dim() == 2 and out.shape[1] == 3 and out.is_contiguous()
+    _check(lib().qi_clock_probe(_ptr(out), int(out.shape[0]), int(iters), _stream()))
+
+
+def wall_clock_khz(device: int = 0) -> int:
+    khz = int(lib().qi_wall_clock_khz(int(device)))
+    if khz <= 0:
+        raise QiError(7, last_error())
+    return khz

@@ -13,6 +13,10 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqi.so")
+# the strict probe alone, built with -ffast-math: its verdict on a GPU must
+# be the strict failure (the probe detects a relaxed build)
+PROBE_SRC = os.path.join(CSRC, "probe", "qi_probe_lib.hip")
+PROBE_FASTMATH_LIB = os.path.join(PKG, "libqi_probe_fastmath.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -36,14 +40,22 @@ def sources() -> list:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source of the library into libqi.so (always)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, *sources(), "-o", tmp]
+def _compile(srcs, out, flags, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *flags, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source of the library into libqi.so, and the probe
+    alone with -ffast-math into libqi_probe_fastmath.so (always)."""
+    _compile(sources(), LIB, [*FLAGS, *extra_flags], verbose)
+    # -ffast-math after the strict flags overrides them (fast math, FP
+    # contraction, finite-math assumptions)
+    _compile([PROBE_SRC], PROBE_FASTMATH_LIB, [*FLAGS, "-ffast-math"], verbose)
     return LIB
 
 

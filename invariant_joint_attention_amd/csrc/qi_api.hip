@@ -25,6 +25,7 @@
 #include "../../include/qi.h"
 #include "qi_common.h"
 #include "qi_kernels.h"
+#include "qi_probe.h"
 
 using namespace qi;
 
@@ -127,24 +128,37 @@ int check_alias(const std::vector<Extent>& ext) {
 }
 
 // ------------------------------------------------- device gate and probe
-__device__ uint32_t g_probe_out[8];
-
-__global__ void strict_probe_kernel(float sub, float three, float two, float tie1, float tie2, float zero,
-                                    float x, float y) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  g_probe_out[0] = __float_as_uint(sub * 1.5f);   // subnormal survives (no flush)
-  g_probe_out[1] = __float_as_uint(1.0f / three); // correctly rounded division
-  g_probe_out[2] = __float_as_uint(sqrtf(two));   // correctly rounded square root
-  g_probe_out[3] = pack_bf16x2(tie1, tie2);       // FP32 -> BF16 ties to even
-  g_probe_out[4] = __float_as_uint(__builtin_amdgcn_exp2f(zero));  // exp2(0) == 1 exactly
-  const float prod = x * x;                        // no contraction into an fma
-  g_probe_out[5] = __float_as_uint(prod - y);
-}
-
-uint32_t f2u(float f) {
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  return u;
+// Shader-clock probe for measurement: each single-wave workgroup reads the
+// shader clock counter (s_memtime) and the constant-rate wall clock
+// (s_memrealtime), runs `iters` rounds of four independent BF16 MFMAs (a
+// matrix load like the attention kernel's), reads both again and writes
+// the two differences.  Both readings of a pair come from the same wave, so
+// counters of different XCDs are never subtracted from each other.
+__global__ void clock_probe_kernel(unsigned long long* out, int iters, float seed) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (float)(threadIdx.x + i));
+    b[i] = (__bf16)(seed * (float)(i - (int)threadIdx.x));
+  }
+  f32x16 acc[4] = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = mfma32(a, b, acc[j]);
+  }
+  float sink = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sink += acc[j][0];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    unsigned long long* o = out + 3 * (size_t)blockIdx.x;
+    o[0] = t1 - t0;
+    o[1] = r1 - r0;
+    o[2] = (unsigned long long)__float_as_uint(sink);
+  }
 }
 
 std::mutex g_mu;
@@ -152,24 +166,9 @@ std::map<int, int> g_dev_status;     // device id -> QI_OK / error code
 std::map<int, std::string> g_dev_msg;
 
 int run_probe(int dev) {
-  const float sub = std::ldexp(1.0f, -140), three = 3.0f, two = 2.0f;
-  const float tie1 = 1.0f + std::ldexp(1.0f, -8), tie2 = 1.0f + 3.0f * std::ldexp(1.0f, -8);
-  const float x = 1.0f + std::ldexp(1.0f, -12), y = 1.0f + std::ldexp(1.0f, -11);
-  hipLaunchKernelGGL(strict_probe_kernel, dim3(1), dim3(64), 0, 0, sub, three, two, tie1, tie2, 0.0f, x, y);
-  if (hipGetLastError() != hipSuccess) return fail(QI_E_HIP, "strict probe launch failed on device %d", dev);
-  uint32_t out[8] = {0};
-  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_probe_out), sizeof out, 0, hipMemcpyDeviceToHost) != hipSuccess)
-    return fail(QI_E_HIP, "strict probe readback failed on device %d", dev);
-  volatile float vthree = three, vtwo = two;
-  const uint32_t want[6] = {f2u(std::ldexp(3.0f, -141)), f2u(1.0f / vthree), f2u(std::sqrt(vtwo)),
-                            0x3F823F80u, f2u(1.0f), 0u};
-  const char* what[6] = {"subnormal multiply", "division rounding", "sqrt rounding", "bf16 RNE",
-                         "exp2(0)", "no fma contraction"};
-  for (int i = 0; i < 6; ++i)
-    if (out[i] != want[i])
-      return fail(QI_E_STRICT, "strict probe failed on device %d: %s (got 0x%08x want 0x%08x)", dev, what[i],
-                  out[i], want[i]);
-  return QI_OK;
+  char msg[256];
+  const int rc = probe::run(dev, msg, sizeof msg);
+  return rc ? fail(rc, "%s", msg) : QI_OK;
 }
 
 int gate_device(int dev) {
@@ -976,6 +975,27 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
   float* const dg_ps[2] = {dgain_q_ps, dgain_k_ps};
   float* const dg[2] = {dgain_q, dgain_k};
   return launch_prologue_bwd(geom, xs, gains, dxs, parts, dg_ps, dg, Lw, stream);
+}
+
+int qi_clock_probe(uint64_t* out, int32_t n_groups, int32_t iters, hipStream_t stream) {
+  if (!out) return fail(QI_E_INVALID, "out is null");
+  if ((uintptr_t)out % 8) return fail(QI_E_ALIGN, "out is not 8-byte aligned");
+  if (n_groups < 1 || n_groups > 65536) return fail(QI_E_INVALID, "n_groups %d outside 1..65536", n_groups);
+  if (iters < 1 || iters > (1 << 20)) return fail(QI_E_INVALID, "iters %d outside 1..2^20", iters);
+  int rc = current_device_gate();
+  if (rc) return rc;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)n_groups), dim3(64), 0, stream, (unsigned long long*)out,
+                     (int)iters, 1.0f / 1024.0f);
+  return launched("clock_probe_kernel");
+}
+
+int64_t qi_wall_clock_khz(int device) {
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) {
+    fail(QI_E_HIP, "cannot query the wall-clock rate of device %d", device);
+    return 0;
+  }
+  return khz;
 }
 
 const char* qi_trace(void) {

@@ -395,3 +395,21 @@ def test_backward_head_limit_and_workspace_parts():
     rc = L.qi_joint_attn_bwd(g.ptr(), *views, region(6), fake_bshd(region(7), g.B, g.S, g.H), region(8), region(9),
                              *grads, region(14), region(15), None, None, region(20), ws, None)
     assert rc == code("QI_E_UNSUPPORTED") and "65535" in qi.last_error(), qi.last_error()
+
+
+def test_clock_probe_validation():
+    L = qi.lib()
+    assert L.qi_clock_probe(None, 4, 8, None) == code("QI_E_INVALID")
+    assert L.qi_clock_probe(region(0) + 4, 4, 8, None) == code("QI_E_ALIGN")
+    assert L.qi_clock_probe(region(0), 0, 8, None) == code("QI_E_INVALID")
+    assert L.qi_clock_probe(region(0), 4, 0, None) == code("QI_E_INVALID")
+    assert L.qi_clock_probe(region(0), 4, 8, None) == code("QI_E_UNSUPPORTED")  # no device here
+
+
+def test_fast_math_probe_library_is_built_beside_the_library():
+    """build() also writes the probe alone compiled with -ffast-math; the GPU
+    tests expect its verdict to be the strict failure."""
+    path = os.path.join(os.path.dirname(qi.LIB_PATH), "libqi_probe_fastmath.so")
+    assert os.path.exists(path)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert re.search(r"\bT qi_probe_standalone\b", out)

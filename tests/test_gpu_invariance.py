@@ -147,3 +147,61 @@ def test_backward_replay_and_batch():
     two = backward(g2, geo2)
     for n in ("dq", "dk", "dv", "dgain_q_ps", "dgain_k_ps"):
         assert (bits(two[n][:1]) == ref_bits[n]).all(), f"{n}: sample 0 at B=2 differs from B=1"
+
+
+def _bwd_from(g, geo, q=None, k=None):
+    """Forward (prologues + attention, keeping the FP32 O) and backward; q, k
+    replace the prologue outputs the backward consumes when given."""
+    q0, k0, o, lse, of = qi.joint_attention(g["q"], g["k"], g["v"], g["g_q"], g["g_k"], geo, keep_f32=True)
+    q = q0 if q is None else q
+    k = k0 if k is None else k
+    r = qi.joint_attn_bwd(g["q"], g["k"], q, k, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo)
+    torch.cuda.synchronize()
+    return (q0, k0), r
+
+
+def test_backward_padding_invariance():
+    """Re-padding the text to T_txt = 219, 300 and 512 (new pad rows drawn from
+    another seed, dO = 0 on every padded query row) leaves dq, dk, dv of the
+    valid text rows and of the image rows, and the per-sample gain
+    gradients, bit for bit unchanged: padded queries add exact zeros."""
+    wl = workloads.WORKLOADS["1024sq_bwd"]
+    g = to_dev(workloads.make_inputs(wl))
+    L, T, T_img = wl.txt_len[0], wl.T_txt, wl.h * wl.w
+    g["dO"] = g["dO"].clone()
+    g["dO"][:, L:T] = 0
+    _, base = _bwd_from(g, geom(1, wl.H, T, [L], wl.h, wl.w))
+    filler = to_dev(workloads.make_inputs(workloads.custom("fill", 1, wl.H, 512, [0], 1, 1, 78, backward=True)))
+    filler["dO"] = torch.zeros_like(filler["dO"])
+    for T_new in (L, 300, 512):
+        gn = dict(g)
+        for n in ("q", "k", "v", "dO"):
+            gn[n] = _repad(g[n], L, T, T_new, filler[n])
+        _, r = _bwd_from(gn, geom(1, wl.H, T_new, [L], wl.h, wl.w))
+        for n in ("dq", "dk", "dv"):
+            a, b = base[n], r[n]
+            assert (bits(a[:, :L]) == bits(b[:, :L])).all(), f"{n} text rows, T_txt={T_new}"
+            assert (bits(a[:, T:]) == bits(b[:, T_new:T_new + T_img])).all(), f"{n} image rows, T_txt={T_new}"
+        for n in ("dgain_q_ps", "dgain_k_ps", "dgain_q", "dgain_k"):
+            assert (bits(base[n]) == bits(r[n])).all(), f"{n}, T_txt={T_new}"
+
+
+def test_backward_masked_keys_poisoned():
+    """NaN in the masked text keys of k' and Inf in those rows of V leave every
+    gradient byte unchanged (masked keys are never read by the backward)."""
+    wl = workloads.WORKLOADS["1664x928"]
+    B = 2
+    inp = workloads.make_inputs(workloads.custom("poison_bwd", B, 8, wl.T_txt, wl.txt_len[:B], wl.h, wl.w,
+                                                 31, backward=True))
+    g = to_dev(inp)
+    geo = geom(B, 8, wl.T_txt, wl.txt_len[:B], wl.h, wl.w)
+    (q, k), clean = _bwd_from(g, geo)
+    kp, vp = k.clone(), g["v"].clone()
+    for b, L in enumerate(wl.txt_len[:B]):
+        kp[b, L:wl.T_txt] = float("nan")
+        vp[b, L:wl.T_txt] = float("inf")
+    q0, k0, o, lse, of = qi.joint_attention(g["q"], g["k"], g["v"], g["g_q"], g["g_k"], geo, keep_f32=True)
+    r = qi.joint_attn_bwd(g["q"], g["k"], q0, kp, vp, of, lse, g["dO"], g["g_q"], g["g_k"], geo)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dgain_q_ps", "dgain_k_ps", "dgain_q", "dgain_k"):
+        assert (bits(clean[n]) == bits(r[n])).all(), n

@@ -258,20 +258,27 @@ def test_backward_wide_channel_range_dv(orc):
     mixed_check(f64(r["dv"]) / sn, dv / sn, "dv per channel")
 
 
-def test_backward_full_sampled_head(orc):
+def test_backward_full_config_every_element(orc):
+    """The deterministic backward at 1024^2 (B=2: the workload's sample, then
+    one more drawn next, both with 219 valid text tokens; 24 heads): every
+    element of dq, dk, dv of both samples and the per-sample and folded gain
+    gradients against the FP32 oracle.  The attention gradients are taken at
+    the GPU's own q', k' (the values the backward consumes); the prologue
+    backward runs from the raw inputs."""
     wl = workloads.WORKLOADS["1024sq_bwd"]
-    inp, g = gpu_inputs(wl)
-    geo = geom_of(wl)
+    inp, g = gpu_inputs(wl, extra_samples=1)
+    txt_len = inp["txt_len"]
+    geo = geom_of(wl, txt_len=txt_len, B=2)
     q, k, o, lse, r = _bwd_all(g, geo)
-    h = 5
-    b = 0
-    qn, kn = f64(q)[b:b + 1, :, h:h + 1], f64(k)[b:b + 1, :, h:h + 1]
-    vn, dn = f64(inp["v"].float())[b:b + 1, :, h:h + 1], f64(inp["dO"].float())[b:b + 1, :, h:h + 1]
-    dqp, dkp, dv = orc.attn_bwd(qn, kn, vn, dn, wl.txt_len, wl.T_txt)
-    xq = orc.widen(workloads.bits(inp["q"]))[b:b + 1, :, h:h + 1]
-    xk = orc.widen(workloads.bits(inp["k"]))[b:b + 1, :, h:h + 1]
-    dq, _ = orc.qknorm_rope_bwd(xq, inp["g_q"].numpy(), dqp, wl.T_txt, wl.h, wl.w)
-    dk, _ = orc.qknorm_rope_bwd(xk, inp["g_k"].numpy(), dkp, wl.T_txt, wl.h, wl.w)
-    mixed_check(r["dv"][b:b + 1, :, h:h + 1], dv, "dv head 5")
-    mixed_check(r["dq"][b:b + 1, :, h:h + 1], dq, "dq head 5")
-    mixed_check(r["dk"][b:b + 1, :, h:h + 1], dk, "dk head 5")
+    orc.set_threads(min(16, os.cpu_count() or 1))
+    dqp, dkp, dv = orc.attn_bwd(f64(q), f64(k), f64(inp["v"].float()), f64(inp["dO"].float()), txt_len, wl.T_txt)
+    dq, dgq = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["q"])), inp["g_q"].numpy(), dqp, wl.T_txt, wl.h, wl.w)
+    dk, dgk = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["k"])), inp["g_k"].numpy(), dkp, wl.T_txt, wl.h, wl.w)
+    for b in range(2):
+        mixed_check(r["dv"][b], dv[b], f"dv sample {b}")
+        mixed_check(r["dq"][b], dq[b], f"dq sample {b}")
+        mixed_check(r["dk"][b], dk[b], f"dk sample {b}")
+    mixed_check(r["dgain_q_ps"], dgq, "dgain_q per sample")
+    mixed_check(r["dgain_k_ps"], dgk, "dgain_k per sample")
+    mixed_check(r["dgain_q"], fold_batch(dgq), "dgain_q folded")
+    mixed_check(r["dgain_k"], fold_batch(dgk), "dgain_k folded")

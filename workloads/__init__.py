@@ -155,3 +155,15 @@ def proj_inputs(wl: Workload, streams: int = 2, seed_offset: int = 1000) -> dict
     gq = 1.0 + 0.1 * torch.randn(streams, HEAD_DIM, generator=g, dtype=torch.float32)
     gk = 1.0 + 0.1 * torch.randn(streams, HEAD_DIM, generator=g, dtype=torch.float32)
     return dict(x=x, o=o, w_qkv=w_qkv, w_o=w_o, b_qkv=b_qkv, b_o=b_o, g_q=gq, g_k=gk)
+
+
+def staircase_scores(rows: int, tiles: int, seed: int, jump_lo: float = 63.0, jump_hi: float = 1263.0) -> torch.Tensor:
+    """Raw FP32 scores [1, 1, rows, 64 * tiles] whose tile maxima climb: every
+    key of tile 0 is 0 and every key of tile t > 0 equals the previous tile's
+    value plus a jump drawn uniformly from [jump_lo, jump_hi) (raw units), so
+    every tile moves the running maximum of its row by one drawn jump."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    jumps = jump_lo + (jump_hi - jump_lo) * torch.rand(rows, tiles, generator=g, dtype=torch.float64)
+    jumps[:, 0] = 0.0
+    level = torch.cumsum(jumps, dim=1).to(torch.float32)  # [rows, tiles]
+    return level.repeat_interleave(64, dim=1).reshape(1, 1, rows, 64 * tiles).contiguous()
