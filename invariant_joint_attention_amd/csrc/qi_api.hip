@@ -470,6 +470,24 @@ int launch_prologue_bwd(const qi_geom* g, const qi_bshd x[2], const float* const
   return launched("dgain_fold_kernel");
 }
 
+// Argument checks shared by the two whole-row forward entry points.
+int check_fwd_io(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o, float* lse, float* o_f32,
+                 std::vector<Extent>& ext) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  const int64_t S = seq_len(geom);
+  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+  if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
+  if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  return QI_OK;
+}
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -507,17 +525,9 @@ size_t qi_joint_attn_fwd_workspace(const qi_geom* geom) {
 
 int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o, float* lse,
                       float* o_f32, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int rc = check_geom(geom);
-  if (rc) return rc;
   std::vector<Extent> ext;
-  const int64_t S = seq_len(geom);
-  const int64_t n = (int64_t)geom->B * S * geom->H * kHeadDim;
-  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
-  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
-  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
-  if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
-  if ((rc = check_dense(lse, (int64_t)geom->B * geom->H * S * 4, true, "lse", ext))) return rc;
-  if ((rc = check_dense(o_f32, n * 4, true, "o_f32", ext, true))) return rc;
+  int rc = check_fwd_io(geom, q, k, v, o, lse, o_f32, ext);
+  if (rc) return rc;
   const size_t ws_need = fwd_workspace_bytes(geom);
   if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
   if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
@@ -525,8 +535,6 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
     return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
   ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
   if ((rc = check_alias(ext))) return rc;
-  if (S > 1 && k.ss > kFwdMaxRowStride)
-    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
 
   return launch_fwd(geom, q, k, v, &o, lse, o_f32, (uint16_t*)workspace, nullptr, nullptr, nullptr, nullptr, stream);

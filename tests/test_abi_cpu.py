@@ -413,3 +413,4 @@ def test_fast_math_probe_library_is_built_beside_the_library():
     assert os.path.exists(path)
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     assert re.search(r"\bT qi_probe_standalone\b", out)
+
