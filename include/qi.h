@@ -145,6 +145,25 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
                       hipStream_t stream);
 
 /*
+ * qi_joint_attn_fwd_noalloc -- qi_joint_attn_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument, and the call
+ * allocates and frees nothing.  The V tiles go to a static device array of
+ * the library, 64 MiB (67108864 bytes) per GPU, held from the first call on
+ * that GPU until the process ends.  Geometries whose
+ * qi_joint_attn_fwd_workspace() exceeds 64 MiB (B * H * nt above 4096 key
+ * tiles; the 1024^2 shape at 24 heads needs 1632 per row) return
+ * QI_E_WORKSPACE before anything is launched.  O, LSE and O_f32 equal
+ * qi_joint_attn_fwd's byte for byte; every other argument and error as there.
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and give undefined results; a
+ * call may follow any earlier call on the same stream (each call rewrites
+ * every tile it reads).
+ */
+int qi_joint_attn_fwd_noalloc(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o,
+                              float* lse, float* o_f32, hipStream_t stream);
+
+/*
  * qi_qkv_prologue -- the forward's preparation in one launch: the Q and K
  * prologues of qi_qknorm_rope (same arithmetic, same bytes) and the V ->
  * FP16 key-tile conversion that qi_joint_attn_fwd otherwise runs first.

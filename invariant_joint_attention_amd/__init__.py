@@ -22,7 +22,8 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
           5: "QI_E_WORKSPACE", 6: "QI_E_STRICT", 7: "QI_E_HIP"}
 
 # every entry point declared in include/qi.h
-SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_qkv_prologue",
+SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_fwd_noalloc",
+           "qi_qkv_prologue",
            "qi_joint_attn_fwd_vtiles", "qi_joint_attn_fwd_partial",
            "qi_joint_attn_merge", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
            "qi_joint_attn_key_slots",
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd_workspace.argtypes = [G]
         L.qi_joint_attn_fwd_workspace.restype = ctypes.c_size_t
         L.qi_joint_attn_fwd.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, P, ctypes.c_size_t, S]
+        L.qi_joint_attn_fwd_noalloc.argtypes = [G, QiBshd, QiBshd, QiBshd, QiBshd, P, P, S]
         L.qi_qkv_prologue.argtypes = [G, QiBshd, QiBshd, QiBshd, P, P, QiBshd, QiBshd, P, ctypes.c_size_t, S]
         L.qi_joint_attn_fwd_vtiles.argtypes = [G, QiBshd, QiBshd, P, ctypes.c_size_t, QiBshd, P, P, S]
         L.qi_joint_attn_fwd_partial.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, ctypes.c_size_t, S]
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.qi_last_error.restype = ctypes.c_char_p
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
-        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
+        for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_noalloc", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
                      "qi_qkv_proj", "qi_attn_out_proj",
                      "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
                      "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_clock_probe", "qi_strict_probe"):
@@ -175,6 +177,15 @@ def joint_attn_fwd(q, k, v, geom: Geometry, out=None, lse=None, out_f32=None, wo
     _check(lib().qi_joint_attn_fwd(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
                                    _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream()))
+    return out, lse
+
+
+def joint_attn_fwd_noalloc(q, k, v, geom: Geometry, out, lse, out_f32=None):
+    """qi_joint_attn_fwd_noalloc: the forward with the library's static
+    scratch instead of a workspace; the caller passes every output (nothing
+    is allocated here either)."""
+    _check(lib().qi_joint_attn_fwd_noalloc(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), _bshd(out), _ptr(lse),
+                                           _ptr(out_f32), _stream()))
     return out, lse
 
 

@@ -488,6 +488,34 @@ int check_fwd_io(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o
   return QI_OK;
 }
 
+// Static scratch of qi_joint_attn_fwd_noalloc: the V tiles the forward
+// otherwise keeps in the caller's workspace.  Each device holds its own copy
+// for the life of the process.  In host code `scratch` only names the
+// symbol; its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is passed to
+// kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::map<int, void*> g_scratch_ptr;  // device id -> device address of `scratch`
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(QI_E_UNSUPPORTED, "no HIP device available");
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QI_E_HIP, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return QI_OK;
+}
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -538,6 +566,24 @@ int qi_joint_attn_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_b
   if ((rc = current_device_gate())) return rc;
 
   return launch_fwd(geom, q, k, v, &o, lse, o_f32, (uint16_t*)workspace, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+int qi_joint_attn_fwd_noalloc(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd o, float* lse,
+                              float* o_f32, hipStream_t stream) {
+  std::vector<Extent> ext;
+  int rc = check_fwd_io(geom, q, k, v, o, lse, o_f32, ext);
+  if (rc) return rc;
+  const size_t ws_need = fwd_workspace_bytes(geom);
+  if (ws_need > kNoAllocScratchBytes)
+    return fail(QI_E_WORKSPACE,
+                "this geometry needs %zu bytes of V tiles, more than the %zu-byte static scratch of "
+                "qi_joint_attn_fwd_noalloc; use qi_joint_attn_fwd with a workspace",
+                ws_need, (size_t)kNoAllocScratchBytes);
+  if ((rc = check_alias(ext))) return rc;
+  if ((rc = current_device_gate())) return rc;
+  void* scratch_dev = nullptr;
+  if ((rc = noalloc_scratch(&scratch_dev))) return rc;
+  return launch_fwd(geom, q, k, v, &o, lse, o_f32, (uint16_t*)scratch_dev, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 int qi_qkv_prologue(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd v, const float* gain_q,

@@ -414,3 +414,23 @@ def test_fast_math_probe_library_is_built_beside_the_library():
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     assert re.search(r"\bT qi_probe_standalone\b", out)
 
+
+def test_noalloc_forward_validation():
+    """The no-allocation forward validates like qi_joint_attn_fwd, and a
+    geometry whose V tiles exceed its 64 MiB static scratch is refused
+    before the device gate."""
+    L = qi.lib()
+
+    def call(g, o=None):
+        views = [fake_bshd(region(i), g.B, g.S, g.H) for i in range(3)]
+        o = o or fake_bshd(region(3), g.B, g.S, g.H)
+        return L.qi_joint_attn_fwd_noalloc(g.ptr(), *views, o, region(4), None, None)
+
+    g = geom()
+    assert call(g) == code("QI_E_UNSUPPORTED")  # valid: only the device gate is left
+    assert call(g, o=fake_bshd(region(0), g.B, g.S, g.H)) == code("QI_E_ALIAS")
+    big = qi.Geometry(B=4, H=24, T_txt=512, grid_h=104, grid_w=58, txt_len=[7, 64, 200, 511])
+    assert call(big) == code("QI_E_WORKSPACE")
+    assert "static scratch" in qi.last_error()
+    ok = qi.Geometry(B=1, H=24, T_txt=256, grid_h=64, grid_w=64, txt_len=[219])
+    assert call(ok) == code("QI_E_UNSUPPORTED")
