@@ -24,12 +24,17 @@ value = algorithmic forward FLOPs per step / wall time per step (TFLOP/s),
 with the algorithmic count 4 * D * H * sum_b S * K_b (K_b = valid keys).  For
 a backward workload `fwd_bwd_step` adds the backward's 10 * D * H * sum_b S * K_b
 to the count over the same step time.
-The attention-forward call is also timed alone with HIP events on the
-launch stream (by default one launch of the attention kernel; with
---separate-prologue the V tile pass and the attention kernel back to back);
-that time gives the roofline fraction against the MI355X
-dense BF16 MFMA peak (2.5 PFLOP/s).  The CPU oracle is timed on a bounded
-sample of the same workload on the host cores (cpu_baseline).
+The K timed steps run back to back between one pair of HIP events and the
+host clock (no event inside the region).  The attention-forward call is then
+timed alone on the launch stream: K back-to-back calls between one event
+pair, five repeats (by default one launch of the attention kernel; with
+--separate-prologue the V tile pass and the attention kernel); that time
+gives the roofline fraction against the MI355X dense BF16 MFMA peak
+(2.5 PFLOP/s).  The other measurements of the line (the 1024^2 backward, the
+key-block forward, the projections, the unfused operators) run before the
+headline loop.  The shader clock is sampled with the library's clock probe
+just before and just after the timed steps.  The CPU oracle is timed on a
+bounded sample of the same workload on the host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -128,16 +133,16 @@ class ClockProbe:
     one wave per SIMD runs MFMAs for ~30 us and times them against the
     constant-rate wall clock (both counters read by the same wave)."""
 
-    def __init__(self, qi, torch, groups=1024, iters=512):
+    def __init__(self, qi, torch, groups=1024, iters=512, samples=2):
         self.qi, self.iters = qi, iters
-        self.buf = torch.zeros((groups, 3), dtype=torch.int64, device="cuda:0")
+        self.bufs = [torch.zeros((groups, 3), dtype=torch.int64, device="cuda:0") for _ in range(samples)]
         self.khz = qi.wall_clock_khz(0)
 
-    def sample(self):
-        self.qi.clock_probe(self.buf, self.iters)
+    def sample(self, i):
+        self.qi.clock_probe(self.bufs[i], self.iters)
 
-    def mhz(self):
-        a = self.buf.cpu().numpy().astype("float64")
+    def mhz(self, i):
+        a = self.bufs[i].cpu().numpy().astype("float64")
         ticks, wall = a[:, 0], a[:, 1]
         ok = wall > 0
         if not ok.any():
@@ -215,14 +220,16 @@ def main():
     # long enough for its clock under matrix load to settle before the
     # headline loop starts
     aux = {}
-    if args.bwd_steps > 0 and not wl.backward:
-        aux["attn_bwd"] = bench_bwd(qi, torch, np, workloads, args.bwd_steps)
+    # the backward's inputs first; its timed loop runs last, right before the
+    # headline warmup, so the timed steps follow ~0.1 s of continuous load
+    bwd_case = prepare_bwd(qi, torch, workloads) if args.bwd_steps > 0 and not wl.backward else None
     if args.block_steps > 0:
         aux["blocks"] = bench_blocks(qi, torch, np, wl, geo, qp, kp, g["v"], args.block_steps)
     if args.proj_steps > 0:
         aux["projections"] = bench_proj(qi, torch, np, workloads, wl, args.proj_steps)
     if args.unfused_steps > 0:
         aux["unfused_fwd"] = bench_unfused(qi, torch, np, wl, geo, qp, kp, g["v"], args.unfused_steps)
+    bwd_report = bench_bwd(torch, np, bwd_case, args.bwd_steps) if bwd_case is not None else None
 
     if not args.graph:
         runs = parts
@@ -238,55 +245,57 @@ def main():
                 p()
             graphs.append(gr)
         runs = [gr.replay for gr in graphs]
-    # Two events per step, around the attention call (the prologue of the
-    # next step follows the second one): every event record costs the stream
-    # a few microseconds, so the step carries no more of them than the
-    # attention timing needs.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    j_fwd = names.index("fwd")
+    # The timed steps carry no events of their own: an event record between
+    # two kernels costs the stream several microseconds and has slowed the
+    # kernel after it, so the K steps run back to back between one event pair.
     clock = ClockProbe(qi, torch)
 
-    def step(e=None):
-        for i, r in enumerate(runs):
-            if e is not None and i == j_fwd:
-                e[0].record()
+    def step():
+        for r in runs:
             r()
-            if e is not None and i == j_fwd:
-                e[1].record()
+
+    def region(fn, n):
+        """GPU time per call of `fn` over n back-to-back calls (one event pair)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(args.warmup):
         step()
-    clock.sample()
+    clock.sample(0)
     torch.cuda.synchronize()
-    clock_before = clock.mhz()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
+    e_start.record()
+    for _ in range(args.steps):
+        step()
+    e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock.sample()
-    torch.cuda.synchronize()
-    clock_after = clock.mhz()
+    gpu_step_ms = e_start.elapsed_time(e_end) / args.steps
+    clock.sample(1)
     ms_step = wall * 1e3 / args.steps
+
+    # The dominant kernel alone, right after the timed steps: the attention
+    # call launched back to back K times between one event pair, five such
+    # repeats (mean of the repeats for the roofline; median and min beside
+    # it); the prologue (and backward) the same way.
+    j_fwd = names.index("fwd")
+    fwd_rep = [region(runs[j_fwd], args.steps) for _ in range(5)]
+    fwd_ms = float(np.mean(fwd_rep))
+    fwd_t = fwd_rep
+    pro_ms = region(runs[names.index("pro")], args.steps)
+    bwd_ms = region(runs[names.index("bwd")], max(1, args.steps // 4)) if wl.backward else 0.0
+    torch.cuda.synchronize()
+    clock_before, clock_after = clock.mhz(0), clock.mhz(1)
     out_sha = sha256_of(o, lse)
-
-    fwd_t = [e[0].elapsed_time(e[1]) for e in ev]
-    fwd_ms = float(np.mean(fwd_t))
-
-    def part_ms(fn, n=10):
-        """A part of the step timed on its own after the headline loop."""
-        es = []
-        for _ in range(n):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            es.append((e0, e1))
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in es]))
-
-    pro_ms = part_ms(runs[names.index("pro")])
-    bwd_ms = part_ms(runs[names.index("bwd")]) if wl.backward else 0.0
+    if bwd_report is not None:
+        aux["attn_bwd"] = bwd_report()
+        aux["attn_bwd"]["sha256_outputs"] = sha256_of(*bwd_case["outputs"])
     fwd_flops = wl.fwd_flops()
     value = fwd_flops / (ms_step * 1e-3) / 1e12
     attn_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -350,19 +359,22 @@ def main():
         "env": env,
         "sha256": {"inputs": in_sha, "outputs_o_lse": out_sha},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "attn_fwd": {"ms": round(fwd_ms, 4), "median_ms": round(float(np.median(fwd_t)), 4),
+        "attn_fwd": {"timed": f"5 repeats of {args.steps} back-to-back calls, one event pair each, after the "
+                              "timed steps",
+                     "ms": round(fwd_ms, 4), "median_ms": round(float(np.median(fwd_t)), 4),
                      "min_ms": round(float(np.min(fwd_t)), 4), "max_ms": round(float(np.max(fwd_t)), 4),
                      "tflops": round(attn_tflops, 2),
                      "pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
                      "pct_peak_median": round(100 * fwd_flops / (float(np.median(fwd_t)) * 1e-3) / 1e12
                                               / PEAK_BF16_TFLOPS, 2),
                      "cache_flushed": flushed},
+        "step_gpu_ms": round(gpu_step_ms, 4),
         "shader_clock": {"before_timed_steps": clock_before, "after_timed_steps": clock_after,
                          "how": "per wave: s_memtime ticks / s_memrealtime ticks x wall-clock rate, one wave "
                                 "per SIMD running BF16 MFMAs for ~30 us, sampled just before and just after "
                                 "the timed steps"},
         "prologue": {"calls": "qi_qknorm_rope x 2" if args.separate_prologue else "qi_qkv_prologue (Q, K, V tiles)",
-                     "timed": "10 calls on their own after the timed steps", "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                     "timed": f"{args.steps} back-to-back calls after the timed steps", "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "launch": "hip_graph_replay" if args.graph else "eager",
@@ -378,8 +390,9 @@ def main():
         if isinstance(v_, dict) and "ms" in v_ and k_ in ("blocks", "unfused_fwd"):
             v_["vs_fused"] = round(v_["ms"] / fwd_ms, 3)
         out[k_] = v_
-    out["order"] = ("the other measurements (" + ", ".join(aux) + ") ran before the headline loop; "
-                    "then warmup and the timed steps") if aux else "warmup, then the timed steps"
+    out["order"] = ("the other measurements (" + ", ".join(aux) + ") ran before the headline loop, the "
+                    "backward last, so that the warmup and the timed steps follow continuous load; then "
+                    "the attention call alone and the prologue alone") if aux else "warmup, then the timed steps"
 
     # ---------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
@@ -388,12 +401,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_bwd(qi, torch, np, workloads, steps):
-    """The deterministic backward of the 1024^2 backward workload (same
-    shapes as the forward workload, its own seed, plus dO): the prologues and
-    the forward (keeping the FP32 O) once, then `steps` backward calls, each
-    timed with HIP events on the launch stream against the dense BF16 MFMA
-    peak on the algorithmic count 10 * D * H * S * K."""
+def prepare_bwd(qi, torch, workloads):
+    """Inputs, forward state and buffers of the 1024^2 backward workload
+    (same shapes as the forward workload, its own seed, plus dO): the
+    prologues and the forward (keeping the FP32 O) run once here."""
     dev = "cuda:0"
     wl = workloads.WORKLOADS["1024sq_bwd"]
     inp = workloads.make_inputs(wl)
@@ -405,18 +416,28 @@ def bench_bwd(qi, torch, np, workloads, steps):
     o, lse = qi.joint_attn_fwd(q, k, g["v"], geo, out_f32=of)
     ws = torch.empty(qi.bwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
     grads = {n: torch.empty(q.shape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "dv")}
-    dgq = torch.empty((wl.B, 1, 128), dtype=torch.float32, device=dev)
-    dgk = torch.empty_like(dgq)
-    dgq_f, dgk_f = torch.empty((1, 128), dtype=torch.float32, device=dev), torch.empty((1, 128), dtype=torch.float32,
-                                                                                          device=dev)
+    dg = {n: torch.empty(shape, dtype=torch.float32, device=dev)
+          for n, shape in (("dgain_q_ps", (wl.B, 1, 128)), ("dgain_k_ps", (wl.B, 1, 128)),
+                           ("dgain_q", (1, 128)), ("dgain_k", (1, 128)))}
 
     def run():
         qi.joint_attn_bwd(g["q"], g["k"], q, k, g["v"], of, lse, g["dO"], g["g_q"], g["g_k"], geo, workspace=ws,
-                          dgain_q_ps=dgq, dgain_k_ps=dgk, dgain_q=dgq_f, dgain_k=dgk_f, **grads)
+                          **grads, **dg)
 
-    for _ in range(3):
-        run()
+    run()
     torch.cuda.synchronize()
+    return {"wl": wl, "run": run, "outputs": [grads["dq"], grads["dk"], grads["dv"], dg["dgain_q_ps"],
+                                             dg["dgain_k_ps"]]}
+
+
+def bench_bwd(torch, np, case, steps):
+    """The deterministic backward (qi_joint_attn_bwd) of the prepared 1024^2
+    backward workload, `steps` calls each bracketed by HIP events on the
+    launch stream.  Returns a function that reads the events out later (each
+    read synchronises, so it waits until the headline loop is done) and
+    reports against the dense BF16 MFMA peak on the algorithmic count
+    10 * D * H * S * K."""
+    wl, run = case["wl"], case["run"]
     ev = []
     for _ in range(steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -424,15 +445,17 @@ def bench_bwd(qi, torch, np, workloads, steps):
         run()
         e1.record()
         ev.append((e0, e1))
-    torch.cuda.synchronize()
-    t = [a.elapsed_time(b) for a, b in ev]
-    flops = wl.bwd_flops()
-    ms = float(np.mean(t))
-    return {"workload": f"{wl.name}: {wl.note}", "steps": steps, "calls": "qi_joint_attn_bwd",
-            "ms": round(ms, 4), "median_ms": round(float(np.median(t)), 4), "min_ms": round(float(np.min(t)), 4),
-            "algorithmic_flops": flops, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
-            "sha256_outputs": sha256_of(grads["dq"], grads["dk"], grads["dv"], dgq, dgk)}
+
+    def report():
+        t = [a.elapsed_time(b) for a, b in ev]
+        flops = wl.bwd_flops()
+        ms = float(np.mean(t))
+        return {"workload": f"{wl.name}: {wl.note}", "steps": steps, "calls": "qi_joint_attn_bwd",
+                "ms": round(ms, 4), "median_ms": round(float(np.median(t)), 4), "min_ms": round(float(np.min(t)), 4),
+                "algorithmic_flops": flops, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"}
+
+    return report
 
 
 def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
