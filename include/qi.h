@@ -386,6 +386,13 @@ size_t qi_joint_attn_bwd_workspace(const qi_geom* geom);
  *                  exactly, so dv stays linear in power-of-two factors of dO.
  *   gain_q, gain_k FP32 device [gain_streams][128].
  *   dq, dk, dv     FP32 [B,S,H,128] outputs (dq, dk w.r.t. q_raw, k_raw).
+ *                  Padded text query rows (txt_len[b] <= s < T_txt) are part
+ *                  of the sums over queries of dk and dv like every other
+ *                  row: give them dO = 0 (their outputs carry no gradient;
+ *                  with dO = 0 they add exact zeros, so the valid rows'
+ *                  gradients do not depend on T_txt), and keep their q_raw,
+ *                  k_raw, q, k, o_f32 and lse finite.  Masked keys are never
+ *                  read: their dk, dv rows are exact zeros.
  *   dgain_q_ps, dgain_k_ps   FP32 device [B][gain_streams][128]: gain
  *                  gradients of each sample alone.
  *   dgain_q, dgain_k  nullable FP32 device [gain_streams][128]: the

@@ -20,12 +20,20 @@
 //    Query tiles of 64 rows are visited in a frozen logical order -- valid
 //    text rows from 0, image rows from T_txt, then padded text rows from
 //    L_b -- so the sum over queries of a key never depends on the batch or
-//    the launch.  S = Q K^T and, for dK, dP = dO V^T; then
-//    dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), each
-//    accumulated hi then lo.  Keys of the masked text range get exact zeros.
-// All MFMAs are v_mfma_f32_32x32x16_bf16.  Per accumulator the order is:
-// scores and dP over the 8 head-dim chunks in order; gradients over the
-// 16-row chunks of the streamed side in its frozen order, hi then lo.
+//    the launch.  Padded text query rows take part like every other row:
+//    their dO should be zero (their outputs carry no gradient), and their
+//    q, k, O and LSE must be finite.  S = Q K^T and, for dK, dP = dO V^T;
+//    then dK^T += Q^T (dS_hi + dS_lo), accumulated hi then lo
+//    (v_mfma_f32_32x32x16_bf16), and dV^T += dO16^T P16 with P rounded once
+//    to FP16 and dO as FP16 of dO * 2^e, one power of two per (sample,
+//    head) taken from the slice's largest |dO| (the dQ pass records each
+//    wave's maximum, do_convert_kernel folds them and converts dO), one
+//    v_mfma_f32_32x32x16_f16 per step; dV = acc * 2^-e.  Keys of the masked
+//    text range get exact zeros.
+// Scores, dP, dQ and dK use v_mfma_f32_32x32x16_bf16; dV the f16 form.  Per
+// accumulator the order is: scores and dP over the 8 head-dim chunks in
+// order; gradients over the 16-row chunks of the streamed side in its
+// frozen order (hi then lo for dQ and dK).
 //
 // Schedule (bit-neutral): every pass runs 8-wave workgroups, waves w and
 // w+4 on one SIMD; group 0 (waves 0-3) and group 1 (waves 4-7) alternate,
