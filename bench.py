@@ -389,6 +389,8 @@ def main():
     for k_, v_ in aux.items():
         if isinstance(v_, dict) and "ms" in v_ and k_ in ("blocks", "unfused_fwd"):
             v_["vs_fused"] = round(v_["ms"] / fwd_ms, 3)
+            if "carried" in v_:
+                v_["carried"]["vs_fused"] = round(v_["carried"]["ms"] / fwd_ms, 3)
         out[k_] = v_
     out["order"] = ("the other measurements (" + ", ".join(aux) + ") ran before the headline loop, the "
                     "backward last, so that the warmup and the timed steps follow continuous load; then "
@@ -464,7 +466,9 @@ def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
     partial call per block, then the fixed-order merge; each timed with HIP
     events on the launch stream.  The partial calls together perform the
     whole forward's algorithmic FLOPs; the merge is HBM-bound (it reads n row
-    states of 520 bytes and writes O)."""
+    states of 520 bytes and writes O).  The carried form runs the same blocks
+    as one chain (the state continued in place, the last block writing O
+    and LSE), the ring in which the state travels with the query rows."""
     dev = q.device
     B, H, S, T_img = wl.B, wl.H, wl.S, wl.T_img
     edges = list(range(0, T_img, block)) + [T_img]
@@ -476,7 +480,27 @@ def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     ws = torch.empty(qi.fwd_workspace_bytes(geo), dtype=torch.uint8, device=dev)
-    ev = {"partials": [], "merge": []}
+    ev = {"partials": [], "merge": [], "carried": []}
+    st = (torch.empty((B, H, S, 128), dtype=torch.float32, device=dev),
+          torch.empty((B, H, S), dtype=torch.float32, device=dev),
+          torch.empty((B, H, S, 2), dtype=torch.float32, device=dev))
+    o_c = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse_c = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+
+    def chain(timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)] if timed else None
+        if timed:
+            e[0].record()
+        for i, (wt, lo, hi) in enumerate(blocks):
+            if i + 1 < n:
+                qi.joint_attn_fwd_carry(q, k, v, geo, wt, lo, hi, state=st if i else None, state_out=st,
+                                        workspace=ws)
+            else:
+                qi.joint_attn_fwd_carry(q, k, v, geo, wt, lo, hi, state=st if i else None, last=True, out=o_c,
+                                        lse=lse_c, workspace=ws)
+        if timed:
+            e[1].record()
+            ev["carried"].append((e[0], e[1]))
 
     def run(timed):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
@@ -498,8 +522,15 @@ def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
     for _ in range(steps):
         run(True)
     torch.cuda.synchronize()
+    for _ in range(steps):
+        chain(False)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        chain(True)
+    torch.cuda.synchronize()
     p_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["partials"]]))
     m_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["merge"]]))
+    c_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["carried"]]))
     flops = wl.fwd_flops()
     rows = B * H * S
     m_bytes = n * rows * (128 * 4 + 8) + rows * 128 * 2 + rows * 4
@@ -508,7 +539,10 @@ def bench_blocks(qi, torch, np, wl, geo, q, k, v, steps, block=512):
                          "frac": round(flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"},
             "merge": {"ms": round(m_ms, 4), "bytes": m_bytes, "gbps": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
                       "frac": round(m_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bound": "hbm"},
-            "ms": round(p_ms + m_ms, 4)}
+            "ms": round(p_ms + m_ms, 4),
+            "carried": {"ms": round(c_ms, 4), "tflops": round(flops / (c_ms * 1e-3) / 1e12, 1),
+                        "frac": round(flops / (c_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+                        "state_bytes_per_block": B * H * S * (128 + 3) * 4}}
 
 
 def bench_proj(qi, torch, np, workloads, wl, steps):

@@ -250,6 +250,44 @@ int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc,
                         hipStream_t stream);
 
 /*
+ * qi_joint_attn_fwd_carry -- the forward over one key block continuing the
+ * row state a previous block left: the other ring form of the same rows
+ * ([Kernel list], row joint_attention_fused, Ulysses / Ring sequence
+ * parallelism; [Roadmap], "Numerical requirements").  Where the merge form
+ * keeps every block's state and folds them at the end, here the state
+ * travels from block to block (with the query rows it belongs to) and the
+ * last block writes O and LSE.  The kernel runs the block's key tiles on
+ * the carried (acc, reference max, per-half-wave row sums) exactly as the
+ * whole-row kernel runs them after the tiles before, so a chain of blocks
+ * that visits the keys in the whole call's order -- the text block first,
+ * then image tiles ascending, each block starting where the previous ended
+ * -- gives O, LSE and O_f32 equal byte for byte to qi_joint_attn_fwd, for
+ * any such partition.  Another order gives the same attention within
+ * rounding, not the same bytes.
+ *   q, k, v  as for qi_joint_attn_fwd; block as for qi_joint_attn_fwd_partial.
+ *   acc_in, m_in, l_in   the state to continue, read only: acc FP32 dense
+ *            [B][H][S][128] (16-byte aligned), m FP32 [B][H][S], l FP32
+ *            [B][H][S][2] (8-byte aligned; the two half-wave sums of each
+ *            row).  All three null: the empty state (the first block).
+ *   acc_out, m_out, l_out  the state after the block, same layouts, written;
+ *            each may be the same buffer as its input (continued in place:
+ *            every row reads its state before it writes it), and must not
+ *            overlap anything else.  All three null: this is the last block.
+ *   o, lse, o_f32  written by the last block only (as for
+ *            qi_joint_attn_fwd); pass {NULL} / NULL / NULL otherwise.
+ *   workspace  as for qi_joint_attn_fwd (V tiles of the block).
+ * QI_E_INVALID for a bad block (as qi_joint_attn_fwd_partial), a state given
+ * in part, o / lse / o_f32 on a block that is not the last, or a single
+ * text-only block (no previous state) for a sample with txt_len = 0, whose
+ * rows would have no key.  A chain whose rows saw no key at all writes NaN.
+ */
+int qi_joint_attn_fwd_carry(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v,
+                            qi_key_block block, const float* acc_in, const float* m_in,
+                            const float* l_in, float* acc_out, float* m_out, float* l_out,
+                            qi_bshd o, float* lse, float* o_f32, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Unfused forward -- the three attention operators of [Kernel list], rows
  * joint_attn_qk_gemm, joint_attn_softmax and joint_attn_av_gemm, whose
  * composition qk_gemm -> softmax -> av_gemm gives O, LSE (and O_f32) equal

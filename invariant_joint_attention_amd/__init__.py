@@ -25,7 +25,7 @@ STATUS = {0: "QI_OK", 1: "QI_E_INVALID", 2: "QI_E_UNSUPPORTED", 3: "QI_E_ALIGN",
 SYMBOLS = ("qi_qknorm_rope", "qi_joint_attn_fwd_workspace", "qi_joint_attn_fwd", "qi_joint_attn_fwd_noalloc",
            "qi_qkv_prologue",
            "qi_joint_attn_fwd_vtiles", "qi_joint_attn_fwd_partial",
-           "qi_joint_attn_merge", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
+           "qi_joint_attn_merge", "qi_joint_attn_fwd_carry", "qi_qkv_proj_workspace", "qi_qkv_proj", "qi_attn_out_proj",
            "qi_joint_attn_key_slots",
            "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax", "qi_joint_attn_av_gemm", "qi_joint_attn_bwd_workspace",
            "qi_joint_attn_bwd", "qi_clock_probe", "qi_wall_clock_khz", "qi_last_error", "qi_strict_probe",
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.qi_joint_attn_fwd_vtiles.argtypes = [G, QiBshd, QiBshd, P, ctypes.c_size_t, QiBshd, P, P, S]
         L.qi_joint_attn_fwd_partial.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, ctypes.c_size_t, S]
         L.qi_joint_attn_merge.argtypes = [G, ctypes.c_int32, P, P, P, QiBshd, P, P, S]
+        L.qi_joint_attn_fwd_carry.argtypes = [G, QiBshd, QiBshd, QiBshd, QiKeyBlock, P, P, P, P, P, P, QiBshd, P, P,
+                                              P, ctypes.c_size_t, S]
         L.qi_qkv_proj_workspace.argtypes = [G]
         L.qi_qkv_proj_workspace.restype = ctypes.c_size_t
         L.qi_qkv_proj.argtypes = [G, QiBshd, P, P, ctypes.c_int32, P, P, ctypes.c_int32, QiBshd, QiBshd, QiBshd, P,
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.qi_strict_probe.argtypes = [ctypes.c_int]
         L.qi_trace.restype = ctypes.c_char_p
         for name in ("qi_qknorm_rope", "qi_joint_attn_fwd", "qi_joint_attn_fwd_noalloc", "qi_joint_attn_fwd_partial", "qi_joint_attn_merge",
-                     "qi_qkv_proj", "qi_attn_out_proj",
+                     "qi_joint_attn_fwd_carry", "qi_qkv_proj", "qi_attn_out_proj",
                      "qi_joint_attn_qk_gemm", "qi_joint_attn_softmax",
                      "qi_joint_attn_av_gemm", "qi_joint_attn_bwd", "qi_clock_probe", "qi_strict_probe"):
             getattr(L, name).restype = ctypes.c_int
@@ -230,6 +232,35 @@ def joint_attn_fwd_partial(q, k, v, geom: Geometry, include_text: bool, img_begi
     _check(lib().qi_joint_attn_fwd_partial(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), blk, _ptr(acc), _ptr(m), _ptr(l),
                                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return acc, m, l
+
+
+def joint_attn_fwd_carry(q, k, v, geom: Geometry, include_text: bool, img_begin: int, img_end: int,
+                         state=None, last=False, state_out=None, out=None, lse=None, out_f32=None, workspace=None):
+    """One key block continuing ``state`` = (acc [B,H,S,128], m [B,H,S],
+    l [B,H,S,2]) FP32 (None: the first block).  Not last: returns the state
+    after the block (written to ``state_out``, which may be ``state`` itself
+    for an in-place chain); last: returns (O, LSE) as ``joint_attn_fwd``."""
+    B, H, S = geom.B, geom.H, geom.S
+    if workspace is None:
+        workspace = _empty((max(1, fwd_workspace_bytes(geom)),), torch.uint8, q)
+    blk = QiKeyBlock(int(bool(include_text)), int(img_begin), int(img_end))
+    ins = (None, None, None) if state is None else state
+    no_o = QiBshd(None, 0, 0, 0)
+    if last:
+        outs = (None, None, None)
+        out = _empty(q.shape, torch.bfloat16, q) if out is None else out
+        lse = _empty((B, H, S), torch.float32, q) if lse is None else lse
+        o_arg = _bshd(out)
+    else:
+        outs = state_out if state_out is not None else (
+            _empty((B, H, S, HEAD_DIM), torch.float32, q), _empty((B, H, S), torch.float32, q),
+            _empty((B, H, S, 2), torch.float32, q))
+        o_arg = no_o
+    _check(lib().qi_joint_attn_fwd_carry(geom.ptr(), _bshd(q), _bshd(k), _bshd(v), blk,
+                                         *[_ptr(t) for t in ins], *[_ptr(t) for t in outs], o_arg, _ptr(lse),
+                                         _ptr(out_f32), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream()))
+    return (out, lse) if last else outs
 
 
 def joint_attn_merge(acc, m, l, geom: Geometry, out=None, lse=None, out_f32=None):

@@ -326,12 +326,21 @@ BwdLayout bwd_layout(const qi_geom* g) {
   return L;
 }
 
+// The state a carried key block starts from (all null: the empty state).
+struct CarryIn {
+  const float* acc;
+  const float* m;
+  const float* l;
+};
+
 // One forward call: the V tile pass and the attention kernel per batch chunk.
 // With blk the partial kernel runs over that key block and writes the row
-// state (acc, m, l) instead of O and LSE.
+// state (acc, m, l) instead of O and LSE; with carry as well, the carried
+// kernel continues the state carry holds over the block and writes the new
+// state to (pacc, pm, pl), or O and LSE when pacc is null.
 int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_p, float* lse, float* o_f32,
                uint16_t* vt, const qi_key_block* blk, float* pacc, float* pm, float* pl, hipStream_t stream,
-               bool vt_ready = false) {
+               bool vt_ready = false, const CarryIn* carry = nullptr) {
   int rc;
   const int64_t S = seq_len(geom);
   // vt: FP16 V^T key tiles [B][H][nt_max][128][64] in the workspace
@@ -350,9 +359,14 @@ int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_
     a.blk_text = blk ? blk->include_text : 1;
     a.blk_img_t0 = blk ? blk->img_begin / kFwdBN : 0;
     a.blk_img_t1 = blk ? (int)ceil_div(blk->img_end, kFwdBN) : 0;
+    const int64_t l_words = carry ? 2 : 1;  // carried states keep a row sum per half-wave
     a.pacc = pacc ? pacc + r0 * kHeadDim : nullptr;
     a.pm = pm ? pm + r0 : nullptr;
-    a.pl = pl ? pl + r0 : nullptr;
+    a.pl = pl ? pl + r0 * l_words : nullptr;
+    const bool cin = carry && carry->acc;
+    a.cin_acc = cin ? carry->acc + r0 * kHeadDim : nullptr;
+    a.cin_m = cin ? carry->m + r0 : nullptr;
+    a.cin_l = cin ? carry->l + r0 * 2 : nullptr;
     a.B = nb;
     a.S = (int)S;
     a.H = geom->H;
@@ -381,7 +395,10 @@ int launch_fwd(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_bshd* o_
     }
 
     const int64_t grid = (int64_t)nb * geom->H * a.n_qtiles;
-    if (blk) {
+    if (carry) {
+      hipLaunchKernelGGL(attn_fwd_carry_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
+      if ((rc = launched("attn_fwd_carry_kernel"))) return rc;
+    } else if (blk) {
       hipLaunchKernelGGL(attn_fwd_partial_kernel, dim3((unsigned)grid), dim3(kFwdWaves * 64), 0, stream, a);
       if ((rc = launched("attn_fwd_partial_kernel"))) return rc;
     } else {
@@ -662,11 +679,8 @@ int qi_joint_attn_fwd_vtiles(const qi_geom* geom, qi_bshd q, qi_bshd k, const vo
                     true);
 }
 
-int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_key_block blk, float* acc,
-                              float* m, float* l, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int rc = check_geom(geom);
-  if (rc) return rc;
-  const int64_t S = seq_len(geom), T_img = (int64_t)geom->grid_h * geom->grid_w;
+int check_key_block(const qi_geom* geom, const qi_key_block& blk) {
+  const int64_t T_img = (int64_t)geom->grid_h * geom->grid_w;
   if (blk.include_text != 0 && blk.include_text != 1)
     return fail(QI_E_INVALID, "include_text=%d must be 0 or 1", blk.include_text);
   if (blk.img_begin < 0 || blk.img_begin > blk.img_end || blk.img_end > T_img)
@@ -676,6 +690,25 @@ int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd
     return fail(QI_E_INVALID, "image key range [%d, %d) is not aligned to the 64-key tiles", blk.img_begin,
                 blk.img_end);
   if (!blk.include_text && blk.img_begin == blk.img_end) return fail(QI_E_INVALID, "empty key block");
+  return QI_OK;
+}
+
+int check_workspace(const qi_geom* geom, void* workspace, size_t workspace_bytes, std::vector<Extent>& ext) {
+  const size_t ws_need = fwd_workspace_bytes(geom);
+  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
+  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < ws_need)
+    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
+  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
+  return QI_OK;
+}
+
+int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_key_block blk, float* acc,
+                              float* m, float* l, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  if ((rc = check_key_block(geom, blk))) return rc;
+  const int64_t S = seq_len(geom);
   std::vector<Extent> ext;
   const int64_t rows = (int64_t)geom->B * geom->H * S;
   if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
@@ -684,17 +717,63 @@ int qi_joint_attn_fwd_partial(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd
   if ((rc = check_dense(acc, rows * kHeadDim * 4, true, "acc", ext))) return rc;
   if ((rc = check_dense(m, rows * 4, true, "m", ext, false, 4))) return rc;  // one word per row
   if ((rc = check_dense(l, rows * 4, true, "l", ext, false, 4))) return rc;
-  const size_t ws_need = fwd_workspace_bytes(geom);
-  if (!workspace) return fail(QI_E_WORKSPACE, "workspace is null");
-  if ((uintptr_t)workspace % 256) return fail(QI_E_ALIGN, "workspace is not 256-byte aligned");
-  if (workspace_bytes < ws_need)
-    return fail(QI_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, ws_need);
-  ext.push_back({"workspace", (uintptr_t)workspace, (uintptr_t)workspace + ws_need, true});
+  if ((rc = check_workspace(geom, workspace, workspace_bytes, ext))) return rc;
   if ((rc = check_alias(ext))) return rc;
   if (S > 1 && k.ss > kFwdMaxRowStride)
     return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
   if ((rc = current_device_gate())) return rc;
   return launch_fwd(geom, q, k, v, nullptr, nullptr, nullptr, (uint16_t*)workspace, &blk, acc, m, l, stream);
+}
+
+int qi_joint_attn_fwd_carry(const qi_geom* geom, qi_bshd q, qi_bshd k, qi_bshd v, qi_key_block blk,
+                            const float* acc_in, const float* m_in, const float* l_in, float* acc_out, float* m_out,
+                            float* l_out, qi_bshd o, float* lse, float* o_f32, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  if ((rc = check_key_block(geom, blk))) return rc;
+  const int n_in = !!acc_in + !!m_in + !!l_in, n_out = !!acc_out + !!m_out + !!l_out;
+  if (n_in % 3) return fail(QI_E_INVALID, "acc_in, m_in and l_in must be all null or all given");
+  if (n_out % 3) return fail(QI_E_INVALID, "acc_out, m_out and l_out must be all null or all given");
+  const bool last = n_out == 0;
+  if (!last && (o.data || lse || o_f32))
+    return fail(QI_E_INVALID, "o, lse and o_f32 are written by the last block only (acc_out null)");
+  if (last && !n_in && blk.img_begin == blk.img_end)
+    for (int b = 0; b < geom->B; ++b)
+      if (geom->txt_len[b] == 0)
+        return fail(QI_E_INVALID, "sample %d has no key in a single text-only block", b);
+  const int64_t S = seq_len(geom);
+  const int64_t rows = (int64_t)geom->B * geom->H * S;
+  std::vector<Extent> ext;
+  if ((rc = check_view(geom, q, 2, false, "q", ext))) return rc;
+  if ((rc = check_view(geom, k, 2, false, "k", ext))) return rc;
+  if ((rc = check_view(geom, v, 2, false, "v", ext))) return rc;
+  // A state may be continued in place (the same buffer in and out): each row
+  // reads its own state before it writes it.
+  const float* ins[3] = {acc_in, m_in, l_in};
+  float* outs[3] = {acc_out, m_out, l_out};
+  const int64_t bytes[3] = {rows * kHeadDim * 4, rows * 4, rows * 2 * 4};
+  const char* in_names[3] = {"acc_in", "m_in", "l_in"};
+  const char* out_names[3] = {"acc_out", "m_out", "l_out"};
+  const int word[3] = {16, 4, 8};
+  for (int i = 0; i < 3; ++i) {
+    if (outs[i] && (rc = check_dense(outs[i], bytes[i], true, out_names[i], ext, false, word[i]))) return rc;
+    if (ins[i] && ins[i] != outs[i] && (rc = check_dense(ins[i], bytes[i], false, in_names[i], ext, false, word[i])))
+      return rc;
+  }
+  if (last) {
+    if ((rc = check_view(geom, o, 2, true, "o", ext))) return rc;
+    if ((rc = check_dense(lse, rows * 4, true, "lse", ext))) return rc;
+    if ((rc = check_dense(o_f32, rows * kHeadDim * 4, true, "o_f32", ext, true))) return rc;
+  }
+  if ((rc = check_workspace(geom, workspace, workspace_bytes, ext))) return rc;
+  if ((rc = check_alias(ext))) return rc;
+  if (S > 1 && k.ss > kFwdMaxRowStride)
+    return fail(QI_E_UNSUPPORTED, "k sequence stride above %lld elements", (long long)kFwdMaxRowStride);
+  if ((rc = current_device_gate())) return rc;
+  const CarryIn carry{acc_in, m_in, l_in};
+  return launch_fwd(geom, q, k, v, last ? &o : nullptr, lse, o_f32, (uint16_t*)workspace, &blk, acc_out, m_out,
+                    l_out, stream, false, &carry);
 }
 
 int qi_joint_attn_merge(const qi_geom* geom, int32_t n_blocks, const float* acc, const float* m, const float* l,

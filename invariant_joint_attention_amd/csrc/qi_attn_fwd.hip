@@ -255,12 +255,18 @@ __device__ __forceinline__ void sm_block(St& st, int cur_valid, int hh) {
 
 }  // namespace
 
-// The forward over all key tiles of each row (kPartial = false), or over the
-// tiles of one key block with the row state (acc, reference max, row sum)
-// written out instead of O (kPartial = true).  A block's tiles are processed
-// exactly as the whole row's: same order, same arithmetic per tile.
-template <bool kPartial>
+// The forward over all key tiles of each row (kWhole), or over the tiles of
+// one key block: from an empty state with the row state (acc, reference
+// max, row sum) written out instead of O (kBlock), or continuing the state a
+// previous block left (kCarry), then writing that state (acc, reference max
+// and the two half-wave row sums, so that the next block continues exactly)
+// or, after the last block, O and LSE.  A block's tiles are processed exactly
+// as the whole row's: same order, same arithmetic per tile, so blocks carried
+// over the keys in ascending order give the whole-row bytes.
+enum { kWhole = 0, kBlock = 1, kCarry = 2 };
+template <int kMode>
 __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
+  constexpr bool kPartial = kMode != kWhole;
   __shared__ __attribute__((aligned(1024))) char smem[(kKRing + kVRing) * kTileB];
 
   const int lane = threadIdx.x & 63;
@@ -296,6 +302,22 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     for (int r = 0; r < 16; ++r) st.acc[d][r] = 0.f;
   st.m_used = -INFINITY;
   st.l = 0.f;
+  if constexpr (kMode == kCarry) {
+    if (a.cin_acc && qrow < a.S) {  // the state the previous block left
+      const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
+      const float* prow = a.cin_acc + row * kHeadDim;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 x = *(const f32x4*)(prow + 32 * d + 8 * g4 + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.acc[d][4 * g4 + e] = x[e];
+        }
+      st.m_used = a.cin_m[row];
+      st.l = a.cin_l[2 * row + hh];
+    }
+  }
 
   const int ntxt = (L + kFwdBN - 1) / kFwdBN;
   // Tiles processed, in key order: u < ntb are text tiles u; the others are
@@ -310,7 +332,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     else
       return u;
   };
-  if constexpr (kPartial) {
+  if constexpr (kMode == kBlock) {
     if (nt == 0) {  // no key of this row in the block (uniform over the workgroup)
       if (qrow < a.S) {
         const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
@@ -324,6 +346,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
       return;
     }
   }
+  if (kMode != kCarry || nt > 0) {  // a carried block without keys of this row keeps the state
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
   auto kbuf = [&](int j) { return smem + (j % kKRing) * kTileB; };
   auto vbuf = [&](int j) { return smem + kVRingOfs + (j % kVRing) * kTileB; };
@@ -428,11 +451,30 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
     mm_block<true, true>(st, fr, am);
   }
 
+  }
+
   // ---- epilogue
   const uint32_t lu = __float_as_uint(st.l);
   const auto sw = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  if constexpr (kPartial) {
+  if constexpr (kMode == kCarry) {
+    if (a.pacc) {  // not the last block: the state, with each half-wave's row sum
+      if (qrow < a.S) {
+        const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
+        float* prow = a.pacc + row * kHeadDim;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(f32x4*)(prow + 32 * d + 8 * g4 + 4 * hh) =
+                f32x4{st.acc[d][4 * g4], st.acc[d][4 * g4 + 1], st.acc[d][4 * g4 + 2], st.acc[d][4 * g4 + 3]};
+        if (hh == 0) a.pm[row] = st.m_used;
+        a.pl[2 * row + hh] = st.l;
+      }
+      return;
+    }
+  }
+  if constexpr (kMode == kBlock) {
     // the row state: acc (sum_j p_j v_j 2^-8, FP32), reference max, row sum
     if (qrow < a.S) {
       const int64_t row = ((int64_t)b * a.H + h) * a.S + qrow;
@@ -475,8 +517,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs& a) {
 }
 
 
-__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) { attn_fwd_body<false>(a); }
-__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_partial_kernel(FwdArgs a) { attn_fwd_body<true>(a); }
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_kernel(FwdArgs a) { attn_fwd_body<kWhole>(a); }
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_partial_kernel(FwdArgs a) { attn_fwd_body<kBlock>(a); }
+__global__ __launch_bounds__(kFwdWaves * 64, 1) void attn_fwd_carry_kernel(FwdArgs a) { attn_fwd_body<kCarry>(a); }
 
 // V -> FP16 V^T key tiles, one workgroup per (logical key tile t, h, b).
 __global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {

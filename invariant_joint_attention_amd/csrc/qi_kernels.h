@@ -60,7 +60,11 @@ struct FwdArgs {
   int blk_text, blk_img_t0, blk_img_t1;
   float* pacc;  // [B][H][S][128]: sum_j p_j v_j 2^-8 (B of this launch)
   float* pm;    // [B][H][S]: reference max of the raw scores
-  float* pl;    // [B][H][S]: row sum of p
+  float* pl;    // [B][H][S]: row sum of p; carried blocks: [B][H][S][2], one per half-wave
+  // carried blocks only: the state the previous block left (all null: empty)
+  const float* cin_acc;  // [B][H][S][128]
+  const float* cin_m;    // [B][H][S]
+  const float* cin_l;    // [B][H][S][2]
 };
 
 constexpr int kMaxMergeBlocks = 4096;  // key blocks one merge call folds
@@ -112,6 +116,7 @@ __global__ void qknorm_rope_bwd_kernel(PrologueBwdPair p);
 __global__ void dgain_fold_kernel(DgainFoldPair p);
 __global__ void attn_fwd_kernel(FwdArgs a);
 __global__ void attn_fwd_partial_kernel(FwdArgs a);
+__global__ void attn_fwd_carry_kernel(FwdArgs a);
 __global__ void attn_merge_kernel(MergeArgs a);
 
 // V -> FP16 (v * 2^-8) conversion pass of the forward: writes each logical

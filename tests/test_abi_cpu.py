@@ -299,6 +299,55 @@ def test_block_forward_and_merge_validation():
     assert merge(of=region(6) + 16) == code("QI_E_ALIAS")
 
 
+def test_carried_block_forward_validation():
+    """Carried key-block forward: the state is given whole or not at all, it
+    may be continued in place but overlap nothing else, O and LSE belong to
+    the last block only, and a single text-only block is refused for a
+    sample without text keys."""
+    g = geom()  # T_img = 16
+    L = qi.lib()
+    q = fake_bshd(region(0), g.B, g.S, g.H)
+    k = fake_bshd(region(1), g.B, g.S, g.H)
+    v = fake_bshd(region(2), g.B, g.S, g.H)
+    o = fake_bshd(region(3), g.B, g.S, g.H)
+    no_o = qi.QiBshd(None, 0, 0, 0)
+    ws = L.qi_joint_attn_fwd_workspace(g.ptr())
+    st_in = (region(4), region(5), region(6))
+    st_out = (region(7), region(8), region(10))
+
+    def carry(blk=(1, 0, 16), sin=st_in, sout=st_out, o=no_o, lse=None, of=None, ws_ptr=region(9), ws_bytes=ws,
+              gm=g):
+        return L.qi_joint_attn_fwd_carry(gm.ptr(), q, k, v, qi.QiKeyBlock(*blk), *sin, *sout, o, lse, of, ws_ptr,
+                                         ws_bytes, None)
+
+    none3 = (None, None, None)
+    assert carry() == code("QI_E_UNSUPPORTED")  # valid: stops at the device gate
+    assert carry(sin=none3) == code("QI_E_UNSUPPORTED")  # the first block
+    assert carry(sin=st_in, sout=st_in) == code("QI_E_UNSUPPORTED")  # continued in place
+    assert carry(sout=none3, o=o, lse=region(11)) == code("QI_E_UNSUPPORTED")  # the last block
+    assert carry(sin=none3, sout=none3, o=o, lse=region(11)) == code("QI_E_UNSUPPORTED")  # one block for all
+    assert carry(blk=(0, 0, 0)) == code("QI_E_INVALID")  # empty
+    assert carry(blk=(1, 8, 16)) == code("QI_E_INVALID")  # not tile-aligned
+    assert carry(sin=(region(4), None, region(6))) == code("QI_E_INVALID")
+    assert carry(sout=(region(7), region(8), None)) == code("QI_E_INVALID")
+    assert carry(o=o) == code("QI_E_INVALID")  # O on a block that is not the last
+    assert carry(lse=region(11)) == code("QI_E_INVALID")
+    assert carry(sout=none3, o=o, lse=None) == code("QI_E_INVALID")  # the last block needs LSE
+    assert carry(sout=(region(7), region(8), region(10) + 4)) == code("QI_E_ALIGN")  # two words per row
+    assert carry(sin=(region(4) + 8, region(5), region(6))) == code("QI_E_ALIGN")
+    assert carry(sin=(region(7) + 16, region(5), region(6))) == code("QI_E_ALIAS")  # overlaps acc_out, not equal
+    assert carry(sout=(region(7), region(1), region(10))) == code("QI_E_ALIAS")  # m_out over k
+    assert carry(sin=st_in, sout=(region(4), region(6), region(10))) == code("QI_E_ALIAS")  # m_out over l_in
+    assert carry(sout=none3, o=o, lse=region(4)) == code("QI_E_ALIAS")  # lse over the input state
+    assert carry(ws_ptr=None) == code("QI_E_WORKSPACE")
+    assert carry(ws_bytes=ws - 1) == code("QI_E_WORKSPACE")
+    g0 = geom(B=2, txt_len=[5, 0])
+    last_alone = dict(sin=none3, sout=none3, o=fake_bshd(region(3), g0.B, g0.S, g0.H), lse=region(11), gm=g0,
+                      ws_bytes=L.qi_joint_attn_fwd_workspace(g0.ptr()))
+    assert carry(blk=(1, 0, 0), **last_alone) == code("QI_E_INVALID")  # sample 1 would have no key
+    assert carry(blk=(1, 0, 16), **last_alone) == code("QI_E_UNSUPPORTED")
+
+
 def test_projection_validation():
     """QKV and output projections: weights, streams, contiguity of a token's
     channels, outputs and workspace are checked before any launch."""
