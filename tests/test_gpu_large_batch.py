@@ -1,7 +1,8 @@
 """Batches larger than one launch holds (64 rows: the per-row text lengths
 travel in the kernel arguments): the library splits them into launches of up
 to 64 rows, and every row's bytes equal its run alone -- forward, backward,
-the key-block forward with merge, the unfused operators and the projections."""
+the key-block forward with merge, the carried key-block chain, the unfused
+operators and the projections."""
 import pytest
 import torch
 
@@ -115,3 +116,25 @@ def test_qkv_prologue_path_equals_separate_calls(case):
     torch.cuda.synchronize()
     assert _same(qf, q) and _same(kf, k)
     assert _same(of_, o) and _same(lf, lse)
+
+
+def test_carried_chain_over_two_launches(case):
+    """The carried key-block forward at a batch of two launches: text block,
+    then the image keys in two tile-aligned blocks, the state continued in
+    place; every row equals the whole-row forward byte for byte (the state
+    offsets of the second launch included)."""
+    wl, g, geo = case
+    print("large batch: carried chain", flush=True)
+    q = qi.qknorm_rope(g["q"], g["g_q"], geo)
+    k = qi.qknorm_rope(g["k"], g["g_k"], geo)
+    of = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    o, lse = qi.joint_attn_fwd(q, k, g["v"], geo, out_f32=of)
+    st = (torch.full((B, 2, wl.S, 128), float("nan"), dtype=torch.float32, device=DEV),
+          torch.full((B, 2, wl.S), float("nan"), dtype=torch.float32, device=DEV),
+          torch.full((B, 2, wl.S, 2), float("nan"), dtype=torch.float32, device=DEV))
+    assert wl.T_img == 16  # one image tile: split it as [0, 16) after the text block
+    st = qi.joint_attn_fwd_carry(q, k, g["v"], geo, True, 0, 0, state_out=st)
+    of_c = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    o_c, lse_c = qi.joint_attn_fwd_carry(q, k, g["v"], geo, False, 0, wl.T_img, state=st, last=True, out_f32=of_c)
+    torch.cuda.synchronize()
+    assert _same(o_c, o) and _same(lse_c, lse) and _same(of_c, of)
