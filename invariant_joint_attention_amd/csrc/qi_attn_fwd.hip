@@ -526,42 +526,4 @@ __global__ __launch_bounds__(256) void v_tiles_kernel(VtileArgs a) {
   v_tile_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Merge of key-block row states in the fixed block order k = 0, 1, ...:
-// m = max_k m_k; alpha_k = exp2((m_k - m) c); acc = alpha_0 acc_0 + alpha_1
-// acc_1 + ...; l likewise; then the forward's epilogue, O = acc / (l 2^-8)
-// and LSE = (m c + log2 l) ln 2.  With one block alpha_0 = exp2(0) = 1 and
-// the result is the whole-row forward's, bit for bit.  A block without keys
-// for a row (m = -inf, acc = l = 0) gets alpha = 0.  32 lanes per row, 4
-// channels per lane.
-__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (row >= a.rows) return;
-  const int c0 = 4 * (threadIdx.x & 31);
-  float m = -INFINITY;
-  for (int k = 0; k < a.n; ++k) m = fmaxf(m, a.m[k * a.rows + row]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-  for (int k = 0; k < a.n; ++k) {
-    const float al = __builtin_amdgcn_exp2f((a.m[k * a.rows + row] - m) * kC);
-    const f32x4 x = *(const f32x4*)(a.acc + (k * a.rows + row) * kHeadDim + c0);
-    const float lk = a.l[k * a.rows + row];
-    if (k == 0) {
-      for (int e = 0; e < 4; ++e) acc[e] = al * x[e];
-      l = al * lk;
-    } else {
-      for (int e = 0; e < 4; ++e) acc[e] = acc[e] + al * x[e];
-      l = l + al * lk;
-    }
-  }
-  const float l_div = l * kVScale;
-  const int64_t bh = row / a.S;
-  const int qrow = (int)(row - bh * a.S);
-  const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
-  const float o0 = acc[0] / l_div, o1 = acc[1] / l_div, o2 = acc[2] / l_div, o3 = acc[3] / l_div;
-  const u32x2 ov = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-  *(u32x2*)(a.o.row(b, qrow, h) + c0) = ov;
-  if (a.of) *(f32x4*)(a.of + (((int64_t)b * a.S + qrow) * a.H + h) * kHeadDim + c0) = f32x4{o0, o1, o2, o3};
-  if (c0 == 0) a.lse[row] = (m * kC + log2f(l)) * kLn2;
-}
-
 }  // namespace qi
