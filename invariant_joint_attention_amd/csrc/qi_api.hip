@@ -1139,7 +1139,8 @@ const char* qi_trace(void) {
              "\"kernels\":{\"prologue\":\"qknorm_rope_fwd_kernel\",\"prologue_bwd\":\"qknorm_rope_bwd_kernel\","
              "\"dgain_fold\":\"dgain_fold_kernel\",\"attn_fwd_v_tiles\":\"v_tiles_kernel\","
              "\"qkv_prologue\":\"qkv_prologue_kernel\",\"attn_fwd\":\"attn_fwd_kernel\","
-             "\"fwd_partial\":\"attn_fwd_partial_kernel\",\"merge\":\"attn_merge_kernel\","
+             "\"fwd_partial\":\"attn_fwd_partial_kernel\",\"fwd_carry\":\"attn_fwd_carry_kernel\","
+             "\"merge\":\"attn_merge_kernel\","
              "\"qkv_proj\":\"proj_gemm_kernel\",\"out_proj\":\"proj_gemm_kernel\",\"rope_table\":\"rope_table_kernel\","
              "\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
              "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","

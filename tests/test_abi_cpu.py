@@ -42,6 +42,9 @@ def test_trace_is_json_with_the_frozen_contract():
     assert t["split_k"] is False and t["split_kv"] is False and t["atomics"] is False
     assert t["fast_math"] is False and t["fp_contract"] == "off"
     assert t["frozen"]["fwd_key_tile"] == 64
+    # every kernel the trace names is one the library defines (the entry points' launches)
+    for name in ("attn_fwd_kernel", "attn_fwd_partial_kernel", "attn_fwd_carry_kernel", "attn_merge_kernel"):
+        assert name in t["kernels"].values()
 
 
 # Fake, never-dereferenced device addresses (validation only looks at them).
