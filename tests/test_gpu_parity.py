@@ -120,27 +120,23 @@ def test_forward_small(orc, spec):
     abs_check(lse, fw["lse"], "LSE end-to-end", atol=2e-3)
 
 
-def _sample_rows(wl):
-    S, T = wl.S, wl.T_txt
-    rngs = [(0, min(32, S)), (max(0, T - 16), min(S, T + 48)), (max(0, S - 40), S)]
-    return rngs
-
-
 @pytest.mark.parametrize("cfg", ["1024sq", "1328sq_cfg", "1664x928"])
-def test_forward_full_sampled(orc, cfg):
+def test_forward_full_every_element(orc, cfg):
+    """O and LSE of every row of every head of every sample at the full
+    reference shapes, against the oracle over the GPU's own q', k' (the
+    launch configuration the benchmark times)."""
     wl = workloads.WORKLOADS[cfg]
     inp, g = gpu_inputs(wl)
     geo = geom_of(wl)
     q, k, o, lse, _ = _fwd_all(g, geo)
     qn, kn, on, ln = f64(q), f64(k), f64(o), f64(lse)
     vn = f64(inp["v"].float())
-    heads = [0, wl.H // 2, wl.H - 1]
     for b in range(wl.B):
-        for h in heads:
-            for s0, s1 in _sample_rows(wl):
-                ro, rl = orc.attn_fwd_bh(qn[b, :, h], kn[b, :, h], vn[b, :, h], wl.T_txt, wl.txt_len[b], s0, s1)
-                mixed_check(on[b, s0:s1, h], ro, f"O b{b} h{h} rows {s0}:{s1}")
-                abs_check(ln[b, h, s0:s1], rl, f"LSE b{b} h{h} rows {s0}:{s1}")
+        for h in range(wl.H):
+            ro, rl = orc.attn_fwd_bh(qn[b, :, h], kn[b, :, h], vn[b, :, h], wl.T_txt, wl.txt_len[b], 0, wl.S)
+            mixed_check(on[b, :, h], ro, f"O b{b} h{h}")
+            abs_check(ln[b, h], rl, f"LSE b{b} h{h}")
+        print(f"{cfg}: sample {b}, {wl.H} heads x {wl.S} rows checked", flush=True)
 
 
 def test_forward_constant_v_and_scaling():
