@@ -157,7 +157,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the path shards over (batch, head) with no exchange, "
-              "and this build measures one GPU's share; --gpus must be 1", file=sys.stderr)
+              "and the benchmark measures one GPU's share; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
