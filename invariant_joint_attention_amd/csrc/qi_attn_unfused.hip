@@ -87,6 +87,14 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t off32, uint32_t 
                : "s"(lds_addr), "v"(off32), "s"(base)
                : "memory", "m0");
 }
+// dma16 with the non-temporal hint: for the score and P streams, each byte
+// of which is read once.
+__device__ __forceinline__ void dma16_nt(const char* base, uint32_t off32, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(lds_addr), "v"(off32), "s"(base)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 }  // namespace
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(kQkWaves * 64) void attn_qk_kernel(QkArgs a) {
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + (lane >> 4), c = lane & 15;
       const f32x4 v = *(const f32x4*)(stage + r * 256 + 16 * (c ^ (r & 15)));
-      if (row0 + r < a.S) *(f32x4*)(srow0 + (int64_t)r * Kp + kFwdBN * t + 4 * c) = v;
+      if (row0 + r < a.S) __builtin_nontemporal_store(v, (f32x4*)(srow0 + (int64_t)r * Kp + kFwdBN * t + 4 * c));
     }
   }
 }
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(Softma
     const char* src = sbase + (int64_t)t * kFwdBN * 4;
     const uint32_t dst = addr_of(wbuf + (t & 1) * kSmScoreB);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(src, soff[i], dst + 1024u * i);
+    for (int i = 0; i < 8; ++i) dma16_nt(src, soff[i], dst + 1024u * i);
   };
   // this lane's logical chunk 8kb + 2g + hh of row lr sits at chunk (8kb + 2g) ^ (hh ^ swz(lr))
   const uint32_t frag0 = addr_of(wbuf) + (uint32_t)(lr * 256 + 16 * (hh ^ swz(lr)));
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(kSoftmaxWaves * 64) void attn_softmax_kernel(Softma
       const int r = 8 * i + (lane >> 3);
       if (row0 + r < a.S) {
         const int c = (lane & 7) ^ (r & 7);
-        *(u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * c) = po[i];
+        __builtin_nontemporal_store(po[i], (u32x4*)(prow0 + (int64_t)r * Kp + kFwdBN * t + 8 * c));
       }
     }
     if (store && hh == 0) acol[(int64_t)t * a.S] = alpha;
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(kAvWaves * 64) void attn_av_kernel(AvArgs a) {
     const char* src = pbase + (int64_t)t * kFwdBN * 2;
     const uint32_t dst = addr_of(pbuf);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src, poff[i], dst + 1024u * i);
+    for (int i = 0; i < 4; ++i) dma16_nt(src, poff[i], dst + 1024u * i);
     dma4(abase + (int64_t)t * a.S * 4, aoff, addr_of(abuf));
   };
   const uint16_t* const vt_bh = a.vt + bh * a.nt_max * kVtileElems;
