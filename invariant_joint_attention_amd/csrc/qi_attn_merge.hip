@@ -6,7 +6,8 @@
 // matrix and integration plan", "Numerical requirements" (fixed reduction
 // order, one output cast).  The row states come from attn_fwd_partial_kernel
 // (the forward kernel's tile loop over one key block); this pass is
-// HBM-bound: it reads n states of 520 bytes per row and writes O and LSE.
+// HBM-bound: it reads n states of 520 bytes per row (each byte once, so with
+// the non-temporal hint) and writes O and LSE.
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_attn_contract.h"
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
       if (k < a.n) {
         mk[j] = a.m[k * a.rows + row];
         lk[j] = a.l[k * a.rows + row];
-        xk[j] = *(const f32x4*)(a.acc + (k * a.rows + row) * kHeadDim + c0);
+        xk[j] = __builtin_nontemporal_load((const f32x4*)(a.acc + (k * a.rows + row) * kHeadDim + c0));
       }
     }
 #pragma unroll
