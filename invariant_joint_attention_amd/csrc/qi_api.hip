@@ -1080,10 +1080,10 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.n_ktiles = nk_max;
     a.xcd_remap = ((nb * geom->H) % 8) == 0;
     for (int i = 0; i < kMaxBatchPerLaunch; ++i) a.txt_len[i] = i < nb ? geom->txt_len[b0 + i] : 0;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)nb * geom->H * a.n_qtiles)), dim3(kBwdDqWaves * 64), 0,
-                       stream, a);
-    if ((rc = launched("attn_bwd_dq_kernel"))) return rc;
-    {  // dO -> FP16 under the per-(b, h) scale, from the maxima the dQ pass recorded
+    const int64_t n_dq = (int64_t)nb * geom->H * a.n_qtiles;
+    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)n_dq), dim3(kBwdDqWaves * 64), 0, stream, a);
+    if ((rc = launched("attn_bwd_prep_kernel"))) return rc;
+    {  // dO -> FP16 under the per-(b, h) scale, from the recorded maxima
       DoPrepArgs pa;
       pa.dO = a.dO;
       pa.out = const_cast<uint16_t*>(a.do16.p);
@@ -1096,11 +1096,9 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
                          dim3(256), 0, stream, pa);
       if ((rc = launched("do_convert_kernel"))) return rc;
     }
-    const dim3 kv_grid((unsigned)((int64_t)nb * geom->H * a.n_ktiles));
-    hipLaunchKernelGGL(attn_bwd_dk_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
-    if ((rc = launched("attn_bwd_dk_kernel"))) return rc;
-    hipLaunchKernelGGL(attn_bwd_dv_kernel, kv_grid, dim3(kBwdKvWaves * 64), 0, stream, a);
-    if ((rc = launched("attn_bwd_dv_kernel"))) return rc;
+    const int64_t n_kv = (int64_t)nb * geom->H * a.n_ktiles;
+    hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)(2 * n_kv + n_dq)), dim3(kBwdKvWaves * 64), 0, stream, a);
+    if ((rc = launched("attn_bwd_kernel"))) return rc;
   }
   const qi_bshd xs[2] = {q_raw, k_raw}, dxs[2] = {dq, dk};
   const float* const gains[2] = {gain_q, gain_k};
@@ -1143,8 +1141,8 @@ const char* qi_trace(void) {
              "\"merge\":\"attn_merge_kernel\","
              "\"qkv_proj\":\"proj_gemm_kernel\",\"out_proj\":\"proj_gemm_kernel\",\"rope_table\":\"rope_table_kernel\","
              "\"unfused_qk\":\"attn_qk_kernel\",\"unfused_softmax\":\"attn_softmax_kernel\",\"unfused_av\":\"attn_av_kernel\","
-             "\"attn_bwd_dq\":\"attn_bwd_dq_kernel\",\"attn_bwd_dk\":\"attn_bwd_dk_kernel\","
-             "\"attn_bwd_dv\":\"attn_bwd_dv_kernel\",\"bwd_do_prep\":\"do_convert_kernel\"},"
+             "\"attn_bwd_prep\":\"attn_bwd_prep_kernel\",\"attn_bwd\":\"attn_bwd_kernel (dK, dQ, dV workgroups)\","
+             "\"bwd_do_convert\":\"do_convert_kernel\"},"
              "\"mfma\":\"v_mfma_f32_32x32x16_bf16 (fwd P*V and bwd dV: v_mfma_f32_32x32x16_f16)\",\"accumulator\":\"fp32\","
              "\"frozen\":{\"fwd_key_tile\":%d,\"bwd_dq_key_tile\":%d,\"bwd_dkdv_query_tile\":%d,"
              "\"prologue_dgain_chunk\":%d,\"key_order\":\"text tiles from 0, image tiles from T_txt\","

@@ -6,13 +6,14 @@
 // trees, FP32 accumulators, no atomics); [Kernel list] "[RFC] [Qwen-Image]
 // WS1 Single-GPU Kernel List", rows joint_attn_* (forward and backward).
 //
-// Three passes, each output element written by exactly one lane, no atomics:
-//  * dQ pass (query-tile-major, grid as the forward): per wave 32 queries.
-//    D_i = dO_i . O_i is formed first (fixed order) from the forward's FP32
-//    (pre-cast) O -- the BF16 O would move D by ~2^-9 |dO||O| sqrt(128), which
-//    the gain gradients, sums of many cancelling rows, do not tolerate -- and
-//    stored for the key-side passes.  Then over the key tiles in the
-//    forward's logical order: S^T = K Q^T, dP^T = V dO^T,
+// A preparation kernel forms D_i = dO_i . O_i (fixed order) from the
+// forward's FP32 (pre-cast) O -- the BF16 O would move D by
+// ~2^-9 |dO||O| sqrt(128), which the gain gradients, sums of many cancelling
+// rows, do not tolerate -- and records max |dO| per 32 rows.  Then three
+// passes, each output element written by exactly one lane, no atomics, all
+// in one grid (dK workgroups, then dQ, then dV):
+//  * dQ pass (query-tile-major): per wave 32 queries, over the key tiles in
+//    the forward's logical order: S^T = K Q^T, dP^T = V dO^T,
 //    P = exp2(s*c - LSE*log2 e), dS = P (dP - D), dQ^T += K^T dS^T with dS
 //    split into two BF16 terms (hi = bf16(dS), lo = bf16(dS - hi))
 //    accumulated hi then lo.
@@ -26,8 +27,8 @@
 //    then dK^T += Q^T (dS_hi + dS_lo), accumulated hi then lo
 //    (v_mfma_f32_32x32x16_bf16), and dV^T += dO16^T P16 with P rounded once
 //    to FP16 and dO as FP16 of dO * 2^e, one power of two per (sample,
-//    head) taken from the slice's largest |dO| (the dQ pass records each
-//    wave's maximum, do_convert_kernel folds them and converts dO), one
+//    head) taken from the slice's largest |dO| (the preparation kernel
+//    records the maxima, do_convert_kernel folds them and converts dO), one
 //    v_mfma_f32_32x32x16_f16 per step; dV = acc * 2^-e.  Keys of the masked
 //    text range get exact zeros.
 // Scores, dP, dQ and dK use v_mfma_f32_32x32x16_bf16; dV the f16 form.  Per
@@ -71,8 +72,7 @@ __device__ __forceinline__ void split_pack(const float* v, uint32_t* hi, uint32_
   }
 }
 
-__device__ __forceinline__ void decode_bh(const BwdArgs& a, int ntiles, int& b, int& h, int& tile) {
-  const int g = blockIdx.x;
+__device__ __forceinline__ void decode_bh(const BwdArgs& a, int ntiles, int g, int& b, int& h, int& tile) {
   int bh;
   if (a.xcd_remap) {
     const int xcd = g & 7, j = g >> 3;
@@ -256,35 +256,29 @@ __device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[6 * kTileB];  // K tiles [3], V tiles [3]
+// D_i = dO_i . O_i from the forward's FP32 (pre-cast) O, in a fixed order
+// (per lane half: chunk, then channel; then the two halves), and each
+// wave's max |dO| for the dV operand's scale.  Rows as in the dQ pass.
+__global__ __launch_bounds__(kBwdDqWaves * 64) void attn_bwd_prep_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave >> 2, sub = wave & 3;
   const int lr = lane & 31, hh = lane >> 5;
   int b, h, qt;
-  decode_bh(a, a.n_qtiles, b, h, qt);
-  const int L = a.txt_len[b];
+  decode_bh(a, a.n_qtiles, blockIdx.x, b, h, qt);
   const int qrow = qt * (kBwdDqWaves * 32) + wave * 32 + lr;
   const bool qvalid = qrow < a.S;
-
-  GState st;
   float dpart = 0.f;
   uint32_t amax = 0;  // max |dO| of this lane's values, as BF16 magnitude bits (ordered like the values)
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
+    u32x4 zd = {0u, 0u, 0u, 0u};
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
     if (qvalid) {
-      zq = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
       zd = *(const u32x4*)(a.dO.row(b, qrow, h) + 16 * kk + 8 * hh);
       const float* orow = a.o.row(b, qrow, h) + 16 * kk + 8 * hh;
       o0 = *(const f32x4*)orow;
       o1 = *(const f32x4*)(orow + 4);
     }
-    st.b1[kk] = __builtin_bit_cast(bf16x8, zq);
-    st.b2[kk] = __builtin_bit_cast(bf16x8, zd);
-    // D_i = dO_i . O_i (FP32 pre-cast O), fixed order: chunk, then channel
     const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -295,16 +289,44 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
       amax = max(amax, max(zd[w] & 0x7fffu, (zd[w] >> 16) & 0x7fffu));
     }
   }
-  st.D = dpart + __shfl_xor(dpart, 32);
-  // this wave's max |dO| (order-free) for the dV operand's scale
+  const float D = dpart + __shfl_xor(dpart, 32);
+  // this wave's max |dO| (order-free)
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
   if (lane == 0) a.do_amax[(((int64_t)b * a.H + h) * a.n_qtiles + qt) * kBwdDqWaves + wave] = amax;
+  if (qvalid && hh == 0) a.Dvec[((int64_t)b * a.H + h) * a.S + qrow] = D;
+}
+
+namespace {
+
+__device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, sub = wave & 3;
+  const int lr = lane & 31, hh = lane >> 5;
+  int b, h, qt;
+  decode_bh(a, a.n_qtiles, g, b, h, qt);
+  const int L = a.txt_len[b];
+  const int qrow = qt * (kBwdDqWaves * 32) + wave * 32 + lr;
+  const bool qvalid = qrow < a.S;
+
+  GState st;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
+    if (qvalid) {
+      zq = *(const u32x4*)(a.q.row(b, qrow, h) + 16 * kk + 8 * hh);
+      zd = *(const u32x4*)(a.dO.row(b, qrow, h) + 16 * kk + 8 * hh);
+    }
+    st.b1[kk] = __builtin_bit_cast(bf16x8, zq);
+    st.b2[kk] = __builtin_bit_cast(bf16x8, zd);
+  }
   st.lse2 = INFINITY;
+  st.D = 0.f;
   if (qvalid) {
     const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
     st.lse2 = a.lse[li] * kLog2e;
-    if (hh == 0) a.Dvec[li] = st.D;
+    st.D = a.Dvec[li];
   }
 #pragma unroll
   for (int d = 0; d < 4; ++d)
@@ -401,7 +423,6 @@ __global__ __launch_bounds__(kBwdDqWaves * 64, 1) void attn_bwd_dq_kernel(BwdArg
 }
 
 // ------------------------------------------------------------ dK and dV passes
-namespace {
 
 // Query tiles in the frozen order: valid text, image, padded text.
 struct QTiles {
@@ -476,13 +497,13 @@ constexpr int kKvSmem = 6 * kTileB + 2 * 3 * kBwdBM * 4;  // Q[3], dO[3] tiles; 
 // group 1 Q and LSE; dV: group 0 Q and LSE, group 1 dO -- each group waiting
 // for its loads at the end of its next matrix phase.
 template <bool kDk>
-__device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
+__device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2, sub = wave & 3;
   const int lr = lane & 31, hh = lane >> 5;
   int b, h, kt;
-  decode_bh(a, a.n_ktiles, b, h, kt);
+  decode_bh(a, a.n_ktiles, g, b, h, kt);
   const int L = a.txt_len[b];
   const int nkt_txt = (L + kKvKeysPerWG - 1) / kKvKeysPerWG;
   const int nkt_img = (a.T_img + kKvKeysPerWG - 1) / kKvKeysPerWG;
@@ -623,9 +644,21 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dk_kernel(BwdArgs a) {
+// The three passes in one grid: dK workgroups first, then dQ, then dV (the
+// shortest).  Each workgroup runs one pass body; nothing is shared between
+// workgroups, so every output bit is what the pass computes on its own.  One
+// grid instead of three leaves a single partly filled last round.
+static_assert(kBwdKvWaves == kBwdDqWaves && kKvSmem >= 6 * kTileB, "one workgroup shape for the three passes");
+__global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
-  kv_pass<true>(a, smem);
+  const int g = blockIdx.x;
+  const int n_kv = a.B * a.H * a.n_ktiles, n_dq = a.B * a.H * a.n_qtiles;
+  if (g < n_kv)
+    kv_pass<true>(a, smem, g);
+  else if (g < n_kv + n_dq)
+    dq_pass(a, smem, g - n_kv);
+  else
+    kv_pass<false>(a, smem, g - n_kv - n_dq);
 }
 
 // dO for the dV product: FP16 of dO * 2^e with one power of two per (sample,
@@ -663,11 +696,6 @@ __global__ __launch_bounds__(256) void do_convert_kernel(DoPrepArgs a) {
     for (int k = 0; k < 4; ++k) o[k] = attn::pack_f16x2(ldexpf(bf16_lo(v[k]), e), ldexpf(bf16_hi(v[k]), e));
     *(u32x4*)(a.out + (((int64_t)b * a.S + s_) * a.H + h) * kHeadDim + 8 * c) = o;
   }
-}
-
-__global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_dv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
-  kv_pass<false>(a, smem);
 }
 
 }  // namespace qi

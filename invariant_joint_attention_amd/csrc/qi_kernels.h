@@ -92,7 +92,7 @@ struct BwdArgs {
   View<const uint16_t> q, k, v, dO;
   View<const uint16_t> do16;   // FP16 dO * 2^e(b,h), dense [B,S,H,128] (B of this launch), for the dV product
   const float* do_inv_scale;   // [B][H]: 2^-e(b,h)
-  uint32_t* do_amax;           // [B][H][n_qtiles][kBwdDqWaves]: max |dO| bits of each dQ-pass wave's rows
+  uint32_t* do_amax;           // [B][H][n_qtiles][kBwdDqWaves]: max |dO| bits of each prep wave's rows
   View<const float> o;  // FP32 pre-cast forward output
   const float* lse;  // [B,H,S]
   float* Dvec;       // [B,H,S] workspace: rowsum(dO * O)
@@ -208,7 +208,7 @@ __global__ void proj_gemm_kernel(ProjArgs a);
 __global__ void rope_table_kernel(RopeTableArgs a);
 
 // dO -> FP16 dO * 2^e(b,h): one power of two per (sample, head), from the
-// max |dO| that the dQ pass records per wave.
+// max |dO| that the prep kernel records per wave.
 constexpr int kDoConvRows = 64;  // query rows per workgroup of the conversion
 struct DoPrepArgs {
   View<const uint16_t> dO;  // BF16 [B,S,H,128] (B of this launch)
@@ -219,8 +219,10 @@ struct DoPrepArgs {
   int S, H;
 };
 __global__ void do_convert_kernel(DoPrepArgs a);
-__global__ void attn_bwd_dq_kernel(BwdArgs a);
-__global__ void attn_bwd_dk_kernel(BwdArgs a);
-__global__ void attn_bwd_dv_kernel(BwdArgs a);
+// D and the max |dO| per wave (grid: B*H*n_qtiles workgroups of kBwdDqWaves
+// waves), then the dK, dQ and dV passes in one grid of
+// B*H*(2*n_ktiles + n_qtiles) workgroups.
+__global__ void attn_bwd_prep_kernel(BwdArgs a);
+__global__ void attn_bwd_kernel(BwdArgs a);
 
 }  // namespace qi
