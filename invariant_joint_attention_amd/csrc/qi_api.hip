@@ -309,6 +309,18 @@ int launch_proj(const qi_geom* g, qi_bshd x, const void* w, const float* bias, i
   return launched("proj_gemm_kernel");
 }
 
+// Query tiles per (b, h) of the dK/dV passes' frozen order (valid text,
+// image, padded text; 64 rows each), at the sample that needs the most.
+int bwd_nt_do(const qi_geom* g) {
+  const int64_t T_img = (int64_t)g->grid_h * g->grid_w;
+  int64_t n = 0;
+  for (int b = 0; b < g->B; ++b) {
+    const int64_t L = g->txt_len[b];
+    n = std::max(n, ceil_div(L, kBwdBM) + ceil_div(T_img, kBwdBM) + ceil_div(g->T_txt - L, kBwdBM));
+  }
+  return (int)n;
+}
+
 BwdLayout bwd_layout(const qi_geom* g) {
   BwdLayout L;
   const int64_t S = seq_len(g);
@@ -319,7 +331,7 @@ BwdLayout bwd_layout(const qi_geom* g) {
   const size_t part = align256((size_t)g->B * L.n_chunks * kHeadDim * 4);
   L.pk = L.pq + part;
   L.do16 = L.pk + part;
-  L.amax = L.do16 + align256((size_t)g->B * S * g->H * kHeadDim * 2);
+  L.amax = L.do16 + align256((size_t)g->B * g->H * bwd_nt_do(g) * kVtileElems * 2);
   const size_t n_qtiles = (size_t)ceil_div(S, kBwdDqWaves * 32);
   L.scale = L.amax + align256((size_t)g->B * g->H * n_qtiles * kBwdDqWaves * 4);
   L.total = L.scale + align256((size_t)g->B * g->H * 4);
@@ -1046,6 +1058,7 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
   float* inv_scale = (float*)(ws + Lw.scale);
   const int rows_per_wg = kBwdDqWaves * 32;
   const int keys_per_wg = kBwdKvWaves * 32;
+  const int nt_do = bwd_nt_do(geom);
   int nk_max = 0;
   for (int b0 = 0; b0 < geom->B; b0 += kMaxBatchPerLaunch) {
     const int nb = std::min(kMaxBatchPerLaunch, geom->B - b0);
@@ -1055,8 +1068,8 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.v = view_of<const uint16_t>(v, b0);
     a.o = view_of<const float>(o_f32, b0);
     a.dO = view_of<const uint16_t>(d_o, b0);
-    a.do16 = View<const uint16_t>{do16 + (int64_t)b0 * S * geom->H * kHeadDim, S * geom->H * kHeadDim,
-                                  (int64_t)geom->H * kHeadDim, kHeadDim};
+    a.do16t = do16 + (int64_t)b0 * geom->H * nt_do * kVtileElems;
+    a.nt_do = nt_do;
     a.do_inv_scale = inv_scale + (int64_t)b0 * geom->H;
     a.lse = lse + (int64_t)b0 * geom->H * S;
     a.Dvec = Dvec + (int64_t)b0 * geom->H * S;
@@ -1086,14 +1099,18 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     {  // dO -> FP16 under the per-(b, h) scale, from the recorded maxima
       DoPrepArgs pa;
       pa.dO = a.dO;
-      pa.out = const_cast<uint16_t*>(a.do16.p);
+      pa.out = const_cast<uint16_t*>(a.do16t);
       pa.amax = a.do_amax;
       pa.n_amax = a.n_qtiles * kBwdDqWaves;
       pa.inv_scale = inv_scale + (int64_t)b0 * geom->H;
       pa.S = (int)S;
       pa.H = geom->H;
-      hipLaunchKernelGGL(do_convert_kernel, dim3((unsigned)ceil_div(S, kDoConvRows), (unsigned)geom->H, (unsigned)nb),
-                         dim3(256), 0, stream, pa);
+      pa.T_txt = a.T_txt;
+      pa.T_img = a.T_img;
+      pa.nt_do = nt_do;
+      for (int i = 0; i < kMaxBatchPerLaunch; ++i) pa.txt_len[i] = a.txt_len[i];
+      hipLaunchKernelGGL(do_convert_kernel, dim3((unsigned)nt_do, (unsigned)geom->H, (unsigned)nb), dim3(256), 0,
+                         stream, pa);
       if ((rc = launched("do_convert_kernel"))) return rc;
     }
     const int64_t n_kv = (int64_t)nb * geom->H * a.n_ktiles;

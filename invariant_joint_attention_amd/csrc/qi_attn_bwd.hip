@@ -43,7 +43,8 @@
 // the hi/lo split for tile t+1).  Streamed tiles are triple-buffered in LDS
 // and filled by direct global->LDS loads issued in the VALU phase two tiles
 // ahead; transposed operands come from ds_read_b64_tr_b16 on row-major
-// tiles (see qi_lds.h).
+// tiles (see qi_lds.h), except the dV pass's FP16 dO, which do_convert
+// writes already transposed (one ds_read_b128 per fragment).
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_lds.h"
@@ -55,6 +56,7 @@ namespace {
 
 using namespace lds;
 static_assert(kTileRows == kBwdBN && kTileRows == kBwdBM, "backward tiles are LDS tiles");
+static_assert(kVtileElems == kHeadDim * kBwdBM && kVtileElems * 2 == kTileB, "a transposed FP16 dO tile fills one LDS tile");
 
 constexpr float kC = (float)(1.4426950408889634074 / 11.313708498984760390);  // log2(e)/sqrt(128)
 constexpr float kLog2e = 1.4426950408889634074f;
@@ -120,11 +122,13 @@ struct GBases {
 constexpr int kAhead = 2;
 using Ring = bf16x8[kAhead + 1][2];
 
-template <bool kAcc, bool kS, bool kDp>
+// kF16 (dV pass): the gradient's A operand comes from a transposed FP16
+// tile, one ds_read_b128 per fragment instead of two transposing reads.
+template <bool kAcc, bool kS, bool kDp, bool kF16>
 struct Plan {
   static constexpr int nacc = kAcc ? 8 : 0;
   static constexpr int n = nacc + (kS ? (kDp ? 16 : 8) : 0);
-  static constexpr int reads(int k) { return k < n ? (k < nacc ? 4 : 2) : 0; }
+  static constexpr int reads(int k) { return k < n ? (k < nacc ? (kF16 ? 2 : 4) : 2) : 0; }
   static constexpr int later(int k) {  // LDS reads issued after step k's own, before its MFMAs
     int r = 0;
     for (int i = 1; i <= kAhead; ++i) r += reads(k + i);
@@ -132,15 +136,20 @@ struct Plan {
   }
 };
 
-template <bool kAcc, bool kS, bool kDp, int k>
+template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
 __device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
-  using P = Plan<kAcc, kS, kDp>;
+  using P = Plan<kAcc, kS, kDp, kF16>;
   if constexpr (k < P::n) {
     bf16x8* x = f[k % (kAhead + 1)];
     if constexpr (k < P::nacc) {
       constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
-      x[0] = tr_frag<c2, d0>(b.t);
-      x[1] = tr_frag<c2, d1>(b.t);
+      if constexpr (kF16) {
+        x[0] = __builtin_bit_cast(bf16x8, ds_b128<d0 * 32 * kVtRowB>(b.t ^ (uint32_t)(c2 << 5)));
+        x[1] = __builtin_bit_cast(bf16x8, ds_b128<d1 * 32 * kVtRowB>(b.t ^ (uint32_t)(c2 << 5)));
+      } else {
+        x[0] = tr_frag<c2, d0>(b.t);
+        x[1] = tr_frag<c2, d1>(b.t);
+      }
     } else if constexpr (kDp) {
       constexpr int j = k - P::nacc, kk = j >> 1, kb = j & 1;
       x[0] = row_frag<kk, kb>(b.r1);
@@ -155,9 +164,9 @@ __device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
 
 template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
 __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
-  using P = Plan<kAcc, kS, kDp>;
+  using P = Plan<kAcc, kS, kDp, kF16>;
   if constexpr (k < P::n) {
-    g_issue<kAcc, kS, kDp, k + kAhead>(f, b);
+    g_issue<kAcc, kS, kDp, kF16, k + kAhead>(f, b);
     constexpr int later = P::later(k);
     bf16x8* x = f[k % (kAhead + 1)];
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
@@ -187,11 +196,11 @@ __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
   }
 }
 
-template <bool kAcc, bool kS, bool kDp, int k>
+template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
 __device__ __forceinline__ void g_prefetch(Ring& f, const GBases& b) {
   if constexpr (k < kAhead) {
-    g_issue<kAcc, kS, kDp, k>(f, b);
-    g_prefetch<kAcc, kS, kDp, k + 1>(f, b);
+    g_issue<kAcc, kS, kDp, kF16, k>(f, b);
+    g_prefetch<kAcc, kS, kDp, kF16, k + 1>(f, b);
   }
 }
 
@@ -211,7 +220,7 @@ __device__ __forceinline__ void g_matrix(GState& st, GBases b) {
   asm volatile("" : "+v"(b.t), "+v"(b.r1), "+v"(b.r2));
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
-  g_prefetch<kAcc, kS, kDp, 0>(f, b);
+  g_prefetch<kAcc, kS, kDp, kF16, 0>(f, b);
   __builtin_amdgcn_sched_barrier(0);
   g_step<kAcc, kS, kDp, kF16, 0>(st, f, b);
   __builtin_amdgcn_s_setprio(0);
@@ -569,9 +578,11 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
   };
   // each group loads only one of Q and dO: group 0 dO (dK) or Q (dV)
   const bool loads_o = (grp == 0) == kDk;
-  // dO: BF16 for dP (dK); FP16 dO * 2^e for the dV product
-  const View<const uint16_t> dO = kDk ? a.dO : a.do16;
-  const RowOff ro = row_offsets(loads_o ? dO.ss : a.q.ss, lane);
+  // dO: BF16 rows for dP (dK); for the dV product FP16 dO * 2^e as
+  // transposed tiles (128 channel rows x 64 queries, written by do_convert)
+  const RowOff ro = row_offsets(loads_o ? a.dO.ss : a.q.ss, lane);
+  const VtOff vo = vt_offsets(lane);
+  const uint16_t* const dot_bh = a.do16t + ((int64_t)b * a.H + h) * a.nt_do * kVtileElems;
   const int64_t hb = ((int64_t)b * a.H + h) * a.S;  // [b, h] row of LSE and D
   auto load_q = [&](int j) {
     int q0, nq;
@@ -580,10 +591,14 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
     if (sub == 0 && lane < nq) dma4((const char*)(a.lse + hb + q0), 4u * lane, addr_of((const char*)lrow(j)));
   };
   auto load_o = [&](int j) {
-    int q0, nq;
-    qt.bounds(j, q0, nq);
-    load_rows(dO, ro, obuf(j), b, h, q0, nq, sub, lane);
-    if (kDk && sub == 0 && lane < nq) dma4((const char*)(a.Dvec + hb + q0), 4u * lane, addr_of((const char*)drow(j)));
+    if constexpr (kDk) {
+      int q0, nq;
+      qt.bounds(j, q0, nq);
+      load_rows(a.dO, ro, obuf(j), b, h, q0, nq, sub, lane);
+      if (sub == 0 && lane < nq) dma4((const char*)(a.Dvec + hb + q0), 4u * lane, addr_of((const char*)drow(j)));
+    } else {
+      load_vt(dot_bh + (int64_t)j * kVtileElems, vo, obuf(j), sub);
+    }
   };
   auto load_tile = [&](int j) {
     if (loads_o)
@@ -593,7 +608,7 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
   };
   auto bases = [&](int t, bool next) {
     GBases bb;
-    bb.t = tr_base(addr_of(kDk ? qbuf(t) : obuf(t)), lane);
+    bb.t = kDk ? tr_base(addr_of(qbuf(t)), lane) : vt_base(addr_of(obuf(t)), lane);
     bb.r1 = next ? row_base(addr_of(qbuf(t + 1)), lane) : 0;
     bb.r2 = next ? row_base(addr_of(obuf(t + 1)), lane) : 0;
     return bb;
@@ -668,9 +683,17 @@ __global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_kernel(BwdArgs a
 // absolute error <= max|dO| * 2^-39 below (e under its cap).  The maximum is order-free and
 // covers only the slice's own rows, so the scale, like every output bit,
 // depends on nothing outside the (sample, head).
+//
+// One workgroup per query tile t of the dK/dV passes' frozen order (valid
+// text, image, padded text) of one (b, h): the tile's rows are staged in LDS,
+// then written as 128 channel rows of 64 FP16 values, the queries of each
+// 16-row chunk in the dV product's reduction order (position p holds row p
+// with bits 2 and 3 swapped) and zero past the tile's valid count -- the
+// layout of the forward's V^T key tiles, so a fragment is one 16-byte read.
 __global__ __launch_bounds__(256) void do_convert_kernel(DoPrepArgs a) {
   __shared__ uint32_t red[4];
-  const int h = blockIdx.y, b = blockIdx.z;
+  __shared__ uint32_t tl[kBwdBM][kHeadDim / 2 + 1];  // [query][channel pair]; one pad word per row
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + h;
   uint32_t m = 0;
   for (int i = threadIdx.x; i < a.n_amax; i += 256) m = max(m, a.amax[bh * a.n_amax + i]);
@@ -685,16 +708,33 @@ __global__ __launch_bounds__(256) void do_convert_kernel(DoPrepArgs a) {
     (void)frexpf(__uint_as_float(m << 16), &E);
     e = min(15 - E, 100);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.inv_scale[bh] = ldexpf(1.0f, -e);
-  const int r0 = blockIdx.x * kDoConvRows;
-  for (int i = threadIdx.x; i < kDoConvRows * 16; i += 256) {  // 16 chunks of 8 channels per row
-    const int s_ = r0 + (i >> 4), c = i & 15;
-    if (s_ >= a.S) break;
-    const u32x4 v = *(const u32x4*)(a.dO.row(b, s_, h) + 8 * c);
-    u32x4 o;
+  if (t == 0 && threadIdx.x == 0) a.inv_scale[bh] = ldexpf(1.0f, -e);
+  const QTiles qt(a.txt_len[b], a.T_txt, a.T_img);
+  if (t >= qt.count()) return;  // whole workgroup
+  int q0, nq;
+  qt.bounds(t, q0, nq);
+  for (int i = threadIdx.x; i < kBwdBM * 16; i += 256) {  // 16 chunks of 8 channels per row
+    const int r = i >> 4, c = i & 15;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (r < nq) w = *(const u32x4*)(a.dO.row(b, q0 + r, h) + 8 * c);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = attn::pack_f16x2(ldexpf(bf16_lo(v[k]), e), ldexpf(bf16_hi(v[k]), e));
-    *(u32x4*)(a.out + (((int64_t)b * a.S + s_) * a.H + h) * kHeadDim + 8 * c) = o;
+    for (int k = 0; k < 4; ++k) tl[r][4 * c + k] = w[k];
+  }
+  __syncthreads();
+  uint16_t* const out = a.out + (bh * a.nt_do + t) * kVtileElems;
+  for (int i = threadIdx.x; i < kHeadDim * 8; i += 256) {
+    const int d = i >> 3, j = i & 7;  // channel row, 8-query chunk of the row
+    float f[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = 8 * (j & 1) + k;  // position within 16-row chunk j/2
+      const int r = 16 * (j >> 1) + ((p & 3) | (((p >> 3) & 1) << 2) | (((p >> 2) & 1) << 3));
+      const uint32_t w = tl[r][d >> 1];
+      f[k] = ldexpf((d & 1) ? bf16_hi(w) : bf16_lo(w), e);
+    }
+    const u32x4 o = {attn::pack_f16x2(f[0], f[1]), attn::pack_f16x2(f[2], f[3]), attn::pack_f16x2(f[4], f[5]),
+                     attn::pack_f16x2(f[6], f[7])};
+    *(u32x4*)(out + d * kBwdBM + 8 * j) = o;
   }
 }
 

@@ -90,7 +90,8 @@ constexpr int kBwdKvWaves = 8;  // dK and dV passes: waves (x 32 keys) per workg
 
 struct BwdArgs {
   View<const uint16_t> q, k, v, dO;
-  View<const uint16_t> do16;   // FP16 dO * 2^e(b,h), dense [B,S,H,128] (B of this launch), for the dV product
+  const uint16_t* do16t;       // FP16 dO * 2^e(b,h) as transposed query tiles [B][H][nt_do][128][64], for the dV product
+  int nt_do;                   // query tiles per (b, h) in that buffer
   const float* do_inv_scale;   // [B][H]: 2^-e(b,h)
   uint32_t* do_amax;           // [B][H][n_qtiles][kBwdDqWaves]: max |dO| bits of each prep wave's rows
   View<const float> o;  // FP32 pre-cast forward output
@@ -208,15 +209,16 @@ __global__ void proj_gemm_kernel(ProjArgs a);
 __global__ void rope_table_kernel(RopeTableArgs a);
 
 // dO -> FP16 dO * 2^e(b,h): one power of two per (sample, head), from the
-// max |dO| that the prep kernel records per wave.
-constexpr int kDoConvRows = 64;  // query rows per workgroup of the conversion
+// max |dO| that the prep kernel records per wave; written as transposed
+// query tiles of the dK/dV passes' frozen order (grid: nt_do x H x B).
 struct DoPrepArgs {
   View<const uint16_t> dO;  // BF16 [B,S,H,128] (B of this launch)
-  uint16_t* out;            // FP16 dense [B,S,H,128]
+  uint16_t* out;            // FP16 transposed query tiles [B][H][nt_do][128][64]
   const uint32_t* amax;     // [B][H][n_amax]
   int n_amax;               // maxima per (b, h)
   float* inv_scale;         // [B][H]
-  int S, H;
+  int S, H, T_txt, T_img, nt_do;
+  int txt_len[kMaxBatchPerLaunch];
 };
 __global__ void do_convert_kernel(DoPrepArgs a);
 // D and the max |dO| per wave (grid: B*H*n_qtiles workgroups of kBwdDqWaves
