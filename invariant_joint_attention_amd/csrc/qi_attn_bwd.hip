@@ -37,14 +37,15 @@
 // frozen order (hi then lo for dQ and dK).
 //
 // Schedule (bit-neutral): every pass runs 8-wave workgroups, waves w and
-// w+4 on one SIMD; group 0 (waves 0-3) and group 1 (waves 4-7) alternate,
-// one barrier per phase, between a matrix phase (the gradient MFMAs of tile
-// t, then the scores -- and dP -- of tile t+1) and a VALU phase (P, dS and
-// the hi/lo split for tile t+1).  Streamed tiles are triple-buffered in LDS
-// and filled by direct global->LDS loads issued in the VALU phase two tiles
-// ahead; transposed operands come from ds_read_b64_tr_b16 on row-major
-// tiles (see qi_lds.h), except the dV pass's FP16 dO, which do_convert
-// writes already transposed (one ds_read_b128 per fragment).
+// w+4 on one SIMD, group 0 (waves 0-3) and group 1 (waves 4-7).  A wave
+// alternates a VALU block (P, dS and the hi/lo split of tile t) and a
+// matrix block (the gradient MFMAs of tile t, then the scores -- and dP --
+// of tile t+1), with one workgroup barrier per tile that group 1 passes
+// before its VALU block and group 0 between its VALU and matrix blocks.
+// Streamed tiles sit in LDS rings of four, filled by direct global->LDS
+// loads three tiles ahead; transposed operands come from ds_read_b64_tr_b16
+// on row-major tiles (see qi_lds.h), except the dV pass's FP16 dO, which
+// do_convert writes already transposed (one ds_read_b128 per fragment).
 #include "qi_common.h"
 #include "qi_kernels.h"
 #include "qi_lds.h"
@@ -100,6 +101,56 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t off32, uint32_t 
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// Streamed tiles sit in rings of four and are loaded three tiles ahead.
+constexpr int kRing = 4;
+
+// Tile fill that always issues four loads per wave (so a wave's vmcnt
+// arithmetic is exact): wave `sub` of a group fills rows 16*sub..16*sub+15,
+// four rows per load; rows past `nvalid` repeat the last valid row.  Every
+// consumer masks those rows (their P and dS are exact zeros), so their
+// contents never reach an output, and a masked row of the tensor is never
+// read.
+__device__ __forceinline__ void load_rows_rep(const View<const uint16_t>& src, const RowOff& ro, char* dst, int b,
+                                              int h, int row0, int nvalid, int sub, int lane) {
+  const int r0 = 16 * sub;
+  const uint32_t la = addr_of(dst + r0 * kRowB);
+  if (nvalid >= r0 + 16) {
+    const char* base = (const char*)(src.p + (int64_t)b * src.sb + (int64_t)h * src.sh + (int64_t)(row0 + r0) * src.ss);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(base, ro.o[i], la + 4 * i * kRowB);
+  } else {
+    const int rbase = r0 < nvalid ? r0 : nvalid - 1;  // a valid source row
+    const char* base =
+        (const char*)(src.p + (int64_t)b * src.sb + (int64_t)h * src.sh + (int64_t)(row0 + rbase) * src.ss);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kl = 4 * i + (lane >> 4);                // LDS row within the wave's 16
+      const int srow = min(r0 + kl, nvalid - 1) - rbase;  // source row relative to the base, >= 0
+      const int chunk = (lane & 15) ^ swz(kl);
+      dma16(base, (uint32_t)(srow * (uint32_t)src.ss + 8 * chunk) * 2u, la + 4 * i * kRowB);
+    }
+  }
+}
+
+// Wait until at most n of this wave's vector-memory operations are in flight.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(n) : "memory");
+}
+
+// Group g's barrier: if this wave's group (wave-uniform, in an SGPR) is g,
+// wait until at most n of its vector-memory operations are in flight, then
+// s_barrier; other waves skip both.  One asm block, so the compiler sees no
+// branch between the blocks around it (a branch there makes it spill the
+// matrix-phase registers).
+template <int g, int n>
+__device__ __forceinline__ void group_barrier(int grp) {
+  asm volatile("s_cmp_eq_u32 %0, %1\n\ts_cbranch_scc0 2\n\ts_waitcnt vmcnt(%2)\n\ts_barrier"
+               :
+               : "s"(grp), "i"(g), "i"(n)
+               : "memory", "scc");
+}
 
 // ------------------------------------------------------ matrix phase (all passes)
 // State of one wave: 32 rows of the fixed side (queries for dQ, keys for dK
@@ -183,13 +234,17 @@ __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
         st.acc[d1] = mfma32(x[1], __builtin_bit_cast(bf16x8, st.dl[c2]), st.acc[d1]);
       }
     } else if constexpr (kDp) {
+      // the first chunk starts from a zero accumulator operand, so S and dP
+      // are not live during the gradient steps before them
       constexpr int j = k - P::nacc, kk = j >> 1, kb = j & 1;
-      st.s[kb] = mfma32(x[0], st.b1[kk], st.s[kb]);
-      st.dp[kb] = mfma32(x[1], st.b2[kk], st.dp[kb]);
+      const f32x16 z = {};
+      st.s[kb] = mfma32(x[0], st.b1[kk], kk == 0 ? z : st.s[kb]);
+      st.dp[kb] = mfma32(x[1], st.b2[kk], kk == 0 ? z : st.dp[kb]);
     } else {
       constexpr int kk = k - P::nacc;
-      st.s[0] = mfma32(x[0], st.b1[kk], st.s[0]);
-      st.s[1] = mfma32(x[1], st.b1[kk], st.s[1]);
+      const f32x16 z = {};
+      st.s[0] = mfma32(x[0], st.b1[kk], kk == 0 ? z : st.s[0]);
+      st.s[1] = mfma32(x[1], st.b1[kk], kk == 0 ? z : st.s[1]);
     }
     __builtin_amdgcn_sched_barrier(0);
     g_step<kAcc, kS, kDp, kF16, k + 1>(st, f, b);
@@ -206,15 +261,6 @@ __device__ __forceinline__ void g_prefetch(Ring& f, const GBases& b) {
 
 template <bool kAcc, bool kS, bool kDp, bool kF16 = false>
 __device__ __forceinline__ void g_matrix(GState& st, GBases b) {
-  if (kS) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        st.s[kb][r] = 0.f;
-        if (kDp) st.dp[kb][r] = 0.f;
-      }
-  }
   Ring f;
   // opaque copies keep the per-step address XORs inside their steps
   asm volatile("" : "+v"(b.t), "+v"(b.r1), "+v"(b.r2));
@@ -345,24 +391,27 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
   const int ntxt = (L + kBwdBN - 1) / kBwdBN;
   const int nt = ntxt + (a.T_img + kBwdBN - 1) / kBwdBN;
   char* const kbase = smem;
-  char* const vbase = smem + 3 * kTileB;
-  auto kbuf = [&](int j) { return kbase + (j % 3) * kTileB; };
-  auto vbuf = [&](int j) { return vbase + (j % 3) * kTileB; };
+  char* const vbase = smem + kRing * kTileB;
+  auto kbuf = [&](int j) { return kbase + (j % kRing) * kTileB; };
+  auto vbuf = [&](int j) { return vbase + (j % kRing) * kTileB; };
   auto valid_of = [&](int j) {
     int k0, nv;
     dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
     return nv;
   };
   const RowOff ko = row_offsets(a.k.ss, lane), vo = row_offsets(a.v.ss, lane);
+  // Tile j into ring slot j % 4; for j >= nt the last tile again (a load
+  // into a free slot that nothing reads, so every iteration issues the same
+  // loads and the waits are fixed counts).
   auto load_k = [&](int j) {
     int k0, nv;
-    dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
-    load_rows(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
+    dq_bounds(min(j, nt - 1), ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows_rep(a.k, ko, kbuf(j), b, h, k0, nv, sub, lane);
   };
   auto load_v = [&](int j) {
     int k0, nv;
-    dq_bounds(j, ntxt, L, a.T_txt, a.T_img, k0, nv);
-    load_rows(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
+    dq_bounds(min(j, nt - 1), ntxt, L, a.T_txt, a.T_img, k0, nv);
+    load_rows_rep(a.v, vo, vbuf(j), b, h, k0, nv, sub, lane);
   };
   auto bases = [&](int t) {
     GBases bb;
@@ -372,20 +421,25 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
     return bb;
   };
 
-  // prologue: tiles 0 (group 0) and 1 (group 1)
+  // Schedule: one barrier B_t per key tile.  A wave runs VALU(t) (P, dS,
+  // hi/lo split of tile t) then MM(t) (dQ MFMAs of tile t, then S and dP of
+  // tile t+1); group 1 passes B_t before VALU(t), group 0 between VALU(t)
+  // and MM(t), so between B_t and B_{t+1} both groups run MM(t) and a group
+  // that finishes its VALU block starts its MFMAs beside the other's.
+  // MM(t) reads K tile t (transposed) and K, V tiles t+1; no VALU block
+  // reads LDS.  Tiles 0-2 are loaded up front; then V tile t+3 by group 0
+  // before B_t (V tile t-1, in its slot, was last read by MM(t-2)) and K
+  // tile t+3 by group 1 after B_t (K tile t-1 was last read by MM(t-1)).
+  // Each wave issues four loads per iteration, and at B_t it has landed
+  // every load but its latest four (group 0: tile t+3, group 1: tile t+2),
+  // so tile t+1 is visible to all after B_t.
   if (grp == 0) {
-    load_k(0);
-    load_v(0);
-  } else if (nt > 1) {
-    load_k(1);
-    load_v(1);
+    for (int j = 0; j < 3 && j < nt; ++j) load_v(j);
+  } else {
+    for (int j = 0; j < 3 && j < nt; ++j) load_k(j);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   bar();
-
-  // Both groups run the same sequence; group 1 starts one barrier later, so
-  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
-  if (grp == 1) bar();
   {
     GBases b0;
     b0.t = 0;
@@ -393,22 +447,21 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
     b0.r2 = row_base(addr_of(vbuf(0)), lane);
     g_matrix<false, true, true>(st, b0);
   }
-  bar();
+#pragma clang loop unroll(disable)
   for (int t = 0; t + 1 < nt; ++t) {
-    if (t + 2 < nt) {
-      if (grp == 0)
-        load_v(t + 2);
-      else
-        load_k(t + 2);
-    }
+    group_barrier<1, 4>(grp);  // B_t for group 1
+    if (grp == 1)
+      load_k(t + 3);
+    else
+      load_v(t + 3);
     dq_softmax(st, valid_of(t), hh);
-    bar();
+    group_barrier<0, 4>(grp);  // B_t for group 0
     g_matrix<true, true, true>(st, bases(t));
-    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
-    bar();
   }
+  // the last tile
+  group_barrier<1, 0>(grp);
   dq_softmax(st, valid_of(nt - 1), hh);
-  bar();
+  group_barrier<0, 0>(grp);
   {
     GBases bl;
     bl.t = tr_base(addr_of(kbuf(nt - 1)), lane);
@@ -416,7 +469,6 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
     bl.r2 = 0;
     g_matrix<true, false, true>(st, bl);
   }
-  if (grp == 0) bar();
 
   if (qvalid) {
     float* drow = a.dq.row(b, qrow, h);
@@ -499,7 +551,7 @@ __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const f
 }
 
 constexpr int kKvKeysPerWG = kBwdKvWaves * 32;
-constexpr int kKvSmem = 6 * kTileB + 2 * 3 * kBwdBM * 4;  // Q[3], dO[3] tiles; LSE[3], D[3] rows
+constexpr int kKvSmem = 2 * kRing * kTileB + 2 * kRing * kBwdBM * 4;  // Q, dO tile rings; LSE, D row rings
 
 // kDk: dK pass (S, dP, dK^T += Q^T dS); else dV pass (S, dV^T += dO^T P).
 // Loads two tiles ahead in the VALU phase of tile t -- dK: group 0 dO and D,
@@ -564,47 +616,51 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
   const QTiles qt(L, a.T_txt, a.T_img);
   const int nt = qt.count();
   char* const qbase = smem;
-  char* const obase = smem + 3 * kTileB;
-  float* const lbase = (float*)(smem + 6 * kTileB);
-  float* const dbase = lbase + 3 * kBwdBM;
-  auto qbuf = [&](int j) { return qbase + (j % 3) * kTileB; };
-  auto obuf = [&](int j) { return obase + (j % 3) * kTileB; };
-  auto lrow = [&](int j) { return lbase + (j % 3) * kBwdBM; };
-  auto drow = [&](int j) { return dbase + (j % 3) * kBwdBM; };
+  char* const obase = smem + kRing * kTileB;
+  float* const lbase = (float*)(smem + 2 * kRing * kTileB);
+  float* const dbase = lbase + kRing * kBwdBM;
+  auto qbuf = [&](int j) { return qbase + (j % kRing) * kTileB; };
+  auto obuf = [&](int j) { return obase + (j % kRing) * kTileB; };
+  auto lrow = [&](int j) { return lbase + (j % kRing) * kBwdBM; };
+  auto drow = [&](int j) { return dbase + (j % kRing) * kBwdBM; };
   auto nq_of = [&](int j) {
     int q0, nq;
     qt.bounds(j, q0, nq);
     return nq;
   };
-  // each group loads only one of Q and dO: group 0 dO (dK) or Q (dV)
-  const bool loads_o = (grp == 0) == kDk;
-  // dO: BF16 rows for dP (dK); for the dV product FP16 dO * 2^e as
-  // transposed tiles (128 channel rows x 64 queries, written by do_convert)
-  const RowOff ro = row_offsets(loads_o ? a.dO.ss : a.q.ss, lane);
+  // Group 0 loads the tensor read only as score-side rows (dK: dO for dP;
+  // dV: Q for S); group 1 the tensor also read transposed by the gradient
+  // (dK: Q; dV: FP16 dO * 2^e as transposed tiles written by do_convert)
+  // with the tile's LSE (and, for dK, D) row.
+  const RowOff ro = row_offsets((grp == 0) == kDk ? a.dO.ss : a.q.ss, lane);
   const VtOff vo = vt_offsets(lane);
   const uint16_t* const dot_bh = a.do16t + ((int64_t)b * a.H + h) * a.nt_do * kVtileElems;
   const int64_t hb = ((int64_t)b * a.H + h) * a.S;  // [b, h] row of LSE and D
-  auto load_q = [&](int j) {
+  // Tile j into ring slot j % 4; for j >= nt the last tile again (a load
+  // into a free slot that nothing reads, so every iteration issues the same
+  // loads and the waits are fixed counts).
+  auto load_g0 = [&](int j) {
+    const int js = min(j, nt - 1);
     int q0, nq;
-    qt.bounds(j, q0, nq);
-    load_rows(a.q, ro, qbuf(j), b, h, q0, nq, sub, lane);
-    if (sub == 0 && lane < nq) dma4((const char*)(a.lse + hb + q0), 4u * lane, addr_of((const char*)lrow(j)));
+    qt.bounds(js, q0, nq);
+    load_rows_rep(kDk ? a.dO : a.q, ro, kDk ? obuf(j) : qbuf(j), b, h, q0, nq, sub, lane);
   };
-  auto load_o = [&](int j) {
-    if constexpr (kDk) {
-      int q0, nq;
-      qt.bounds(j, q0, nq);
-      load_rows(a.dO, ro, obuf(j), b, h, q0, nq, sub, lane);
-      if (sub == 0 && lane < nq) dma4((const char*)(a.Dvec + hb + q0), 4u * lane, addr_of((const char*)drow(j)));
-    } else {
-      load_vt(dot_bh + (int64_t)j * kVtileElems, vo, obuf(j), sub);
-    }
-  };
-  auto load_tile = [&](int j) {
-    if (loads_o)
-      load_o(j);
+  // Group 1 also loads the tile's LSE (and D) row: wave `sub` its entries
+  // 16*sub .. 16*sub+15, rows past the tile's valid count repeating its last
+  // row (those entries are masked), so each wave issues 4 + 1 (+ 1) loads.
+  auto load_g1 = [&](int j) {
+    const int js = min(j, nt - 1);
+    int q0, nq;
+    qt.bounds(js, q0, nq);
+    if constexpr (kDk)
+      load_rows_rep(a.q, ro, qbuf(j), b, h, q0, nq, sub, lane);
     else
-      load_q(j);
+      load_vt(dot_bh + (int64_t)js * kVtileElems, vo, obuf(j), sub);
+    if (lane < 16) {
+      const uint32_t r = (uint32_t)min(16 * sub + lane, nq - 1);
+      dma4((const char*)(a.lse + hb + q0), 4u * r, addr_of((const char*)(lrow(j) + 16 * sub)));
+      if (kDk) dma4((const char*)(a.Dvec + hb + q0), 4u * r, addr_of((const char*)(drow(j) + 16 * sub)));
+    }
   };
   auto bases = [&](int t, bool next) {
     GBases bb;
@@ -613,15 +669,27 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
     bb.r2 = next ? row_base(addr_of(obuf(t + 1)), lane) : 0;
     return bb;
   };
+  constexpr int kG1Loads = kDk ? 6 : 5;  // group 1's loads per tile
 
-  load_tile(0);
-  if (nt > 1) load_tile(1);
+  // Schedule as in the dQ pass: one barrier B_t per query tile; group 1
+  // passes it before VALU(t) (P and, for dK, dS of tile t from the LSE and D
+  // rows in LDS), group 0 between VALU(t) and MM(t) (the gradient MFMAs of
+  // tile t, then S and dP of tile t+1).  Between B_t and B_{t+1} the LDS
+  // reads are: tile t of group 1's tensor (transposed), tile t+1 of both
+  // tensors (rows), and the LSE/D rows of tiles t and t+1.  Tiles 0-2 up
+  // front; tile t+3 of group 0's tensor before B_t (its slot's previous
+  // tile, t-1, was last read by MM(t-2)), of group 1's tensor and rows
+  // after B_t (last read by MM(t-1) and VALU(t-1)).  At B_t each wave has
+  // landed every load but its latest tile's, so tile t+1 is visible after
+  // B_t.
+  for (int j = 0; j < 3 && j < nt; ++j) {
+    if (grp == 0)
+      load_g0(j);
+    else
+      load_g1(j);
+  }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   bar();
-
-  // Both groups run the same sequence; group 1 starts one barrier later, so
-  // the two groups alternate phases.  Each group runs 2*nt + 1 barriers.
-  if (grp == 1) bar();
   {
     GBases b0;
     b0.t = 0;
@@ -629,19 +697,22 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
     b0.r2 = row_base(addr_of(obuf(0)), lane);
     g_matrix<false, true, kDk>(st, b0);
   }
-  bar();
+#pragma clang loop unroll(disable)
   for (int t = 0; t + 1 < nt; ++t) {
-    if (t + 2 < nt) load_tile(t + 2);
+    group_barrier<1, kG1Loads>(grp);  // B_t for group 1: tile t+2 may stay in flight
+    if (grp == 1)
+      load_g1(t + 3);
+    else
+      load_g0(t + 3);
     kv_softmax<kDk>(st, lrow(t), drow(t), nq_of(t), hh);
-    bar();
+    group_barrier<0, 4>(grp);  // B_t for group 0: tile t+3, issued just now, may stay in flight
     g_matrix<true, true, kDk, !kDk>(st, bases(t, true));
-    __builtin_amdgcn_s_waitcnt(0x0070);  // this group's loads have landed
-    bar();
   }
+  // the last tile
+  group_barrier<1, 0>(grp);
   kv_softmax<kDk>(st, lrow(nt - 1), drow(nt - 1), nq_of(nt - 1), hh);
-  bar();
+  group_barrier<0, 0>(grp);
   g_matrix<true, false, kDk, !kDk>(st, bases(nt - 1, false));
-  if (grp == 0) bar();
 
   if (kvalid) {
     // dK: times 1/sqrt(128); dV: times 2^-e, undoing dO's power-of-two scale (exact)
@@ -663,7 +734,7 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
 // shortest).  Each workgroup runs one pass body; nothing is shared between
 // workgroups, so every output bit is what the pass computes on its own.  One
 // grid instead of three leaves a single partly filled last round.
-static_assert(kBwdKvWaves == kBwdDqWaves && kKvSmem >= 6 * kTileB, "one workgroup shape for the three passes");
+static_assert(kBwdKvWaves == kBwdDqWaves && kKvSmem >= 2 * kRing * kTileB, "one workgroup shape for the three passes");
 __global__ __launch_bounds__(kBwdKvWaves * 64, 1) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kKvSmem];
   const int g = blockIdx.x;
