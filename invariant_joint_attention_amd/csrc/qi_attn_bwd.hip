@@ -511,9 +511,11 @@ struct QTiles {
 };
 
 // P = exp2(s*c - LSE*log2 e) and, for dK, dS = P (dP - D), per query row
-// (register r of block qb holds query 32*qb + 8*(r/4) + 4*hh + r%4); rows
-// past the tile's valid count are exactly 0.  dS is split hi/lo per 16-row
-// chunk; P (dV) is rounded once to FP16.
+// (register r of block qb holds query 32*qb + 8*(r/4) + 4*hh + r%4).  dS of
+// rows past the tile's valid count is exactly 0.  P of those rows is not
+// masked in the dV pass: their Q rows and LSE entries repeat the tile's last
+// valid row, so P lies in [0, 1], and the dO^T columns it meets are zero.
+// dS is split hi/lo per 16-row chunk; P (dV) is rounded once to FP16.
 template <bool kDk>
 __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const float* dd, int nq, int hh) {
 #pragma unroll
@@ -528,10 +530,14 @@ __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const f
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * j + u;
-        const bool valid = q0 + u < nq;
         const float l2 = lv[u] * kLog2e;
-        const float p = valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[qb][r], kC, -l2)) : 0.f;
-        x[r] = kDk ? (valid ? p * (st.dp[qb][r] - dv[u]) : 0.f) : p;
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[qb][r], kC, -l2));
+        if constexpr (kDk) {
+          const bool valid = q0 + u < nq;
+          x[r] = valid ? e * (st.dp[qb][r] - dv[u]) : 0.f;
+        } else {
+          x[r] = e;
+        }
       }
     }
 #pragma unroll
