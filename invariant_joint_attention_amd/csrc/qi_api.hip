@@ -218,7 +218,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dvec, pq, pk, do16, amax, scale, total;
+  size_t dvec, lse2, pq, pk, do16, amax, scale, total;
   int n_txt_chunks, n_chunks;
 };
 
@@ -327,7 +327,8 @@ BwdLayout bwd_layout(const qi_geom* g) {
   L.n_txt_chunks = (int)ceil_div(g->T_txt, kPrologueChunk);
   L.n_chunks = L.n_txt_chunks + (int)ceil_div((int64_t)g->grid_h * g->grid_w, kPrologueChunk);
   L.dvec = 0;
-  L.pq = align256((size_t)g->B * g->H * S * 4);
+  L.lse2 = align256((size_t)g->B * g->H * S * 4);
+  L.pq = L.lse2 + align256((size_t)g->B * g->H * S * 4);
   const size_t part = align256((size_t)g->B * L.n_chunks * kHeadDim * 4);
   L.pk = L.pq + part;
   L.do16 = L.pk + part;
@@ -1053,6 +1054,7 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
 
   char* ws = (char*)workspace;
   float* Dvec = (float*)(ws + Lw.dvec);
+  float* lse2 = (float*)(ws + Lw.lse2);
   uint16_t* do16 = (uint16_t*)(ws + Lw.do16);
   uint32_t* amax = (uint32_t*)(ws + Lw.amax);
   float* inv_scale = (float*)(ws + Lw.scale);
@@ -1073,6 +1075,7 @@ int qi_joint_attn_bwd(const qi_geom* geom, qi_bshd q_raw, qi_bshd k_raw, qi_bshd
     a.do_inv_scale = inv_scale + (int64_t)b0 * geom->H;
     a.lse = lse + (int64_t)b0 * geom->H * S;
     a.Dvec = Dvec + (int64_t)b0 * geom->H * S;
+    a.lse2 = lse2 + (int64_t)b0 * geom->H * S;
     a.dq = view_of<float>(dq, b0);
     a.dk = view_of<float>(dk, b0);
     a.dv = view_of<float>(dv, b0);

@@ -288,7 +288,8 @@ __device__ __forceinline__ void dq_bounds(int t, int ntxt, int L, int T_txt, int
 
 // P = exp2(s*c - LSE*log2 e) (0 for masked keys), dS = P (dP - D), split
 // into hi = bf16(dS), lo = bf16(dS - hi) per 16-key chunk.
-__device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
+template <bool kMask>
+__device__ __forceinline__ void dq_softmax_t(GState& st, int cur_valid, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     float ds[16];
@@ -296,7 +297,8 @@ __device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
     for (int r = 0; r < 16; ++r) {
       // key of register r in block kb: 32*kb + 8*(r/4) + 4*hh + r%4
       const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float p = key < cur_valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[kb][r], kC, -st.lse2)) : 0.f;
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[kb][r], kC, -st.lse2));
+      const float p = !kMask || key < cur_valid ? e : 0.f;
       ds[r] = p * (st.dp[kb][r] - st.D);
     }
 #pragma unroll
@@ -308,12 +310,20 @@ __device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
     }
   }
 }
+// Full tiles (every tile but the last of each key segment) skip the mask.
+__device__ __forceinline__ void dq_softmax(GState& st, int cur_valid, int hh) {
+  if (cur_valid >= kBwdBN)
+    dq_softmax_t<false>(st, cur_valid, hh);
+  else
+    dq_softmax_t<true>(st, cur_valid, hh);
+}
 
 }  // namespace
 
 // D_i = dO_i . O_i from the forward's FP32 (pre-cast) O, in a fixed order
-// (per lane half: chunk, then channel; then the two halves), and each
-// wave's max |dO| for the dV operand's scale.  Rows as in the dQ pass.
+// (per lane half: chunk, then channel; then the two halves), LSE_i * log2(e)
+// for the key-side passes, and each wave's max |dO| for the dV operand's
+// scale.  Rows as in the dQ pass.
 __global__ __launch_bounds__(kBwdDqWaves * 64) void attn_bwd_prep_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -349,7 +359,11 @@ __global__ __launch_bounds__(kBwdDqWaves * 64) void attn_bwd_prep_kernel(BwdArgs
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
   if (lane == 0) a.do_amax[(((int64_t)b * a.H + h) * a.n_qtiles + qt) * kBwdDqWaves + wave] = amax;
-  if (qvalid && hh == 0) a.Dvec[((int64_t)b * a.H + h) * a.S + qrow] = D;
+  if (qvalid && hh == 0) {
+    const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
+    a.Dvec[li] = D;
+    a.lse2[li] = a.lse[li] * kLog2e;
+  }
 }
 
 namespace {
@@ -516,8 +530,8 @@ struct QTiles {
 // masked in the dV pass: their Q rows and LSE entries repeat the tile's last
 // valid row, so P lies in [0, 1], and the dO^T columns it meets are zero.
 // dS is split hi/lo per 16-row chunk; P (dV) is rounded once to FP16.
-template <bool kDk>
-__device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const float* dd, int nq, int hh) {
+template <bool kDk, bool kMask>
+__device__ __forceinline__ void kv_softmax_t(GState& st, const float* lse, const float* dd, int nq, int hh) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float x[16];
@@ -530,11 +544,16 @@ __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const f
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * j + u;
-        const float l2 = lv[u] * kLog2e;
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[qb][r], kC, -l2));
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st.s[qb][r], kC, -lv[u]));  // lv: LSE * log2(e)
         if constexpr (kDk) {
-          const bool valid = q0 + u < nq;
-          x[r] = valid ? e * (st.dp[qb][r] - dv[u]) : 0.f;
+          // row 32*qb + 8*j + u in lanes 0-31, 4 more in lanes 32-63: the
+          // lane mask is uniform, so it is formed with scalar instructions
+          const int rlo = 32 * qb + 8 * j + u;
+          const uint64_t m = (rlo < nq ? 0x00000000ffffffffull : 0ull) | (rlo + 4 < nq ? 0xffffffff00000000ull : 0ull);
+          const float v = e * (st.dp[qb][r] - dv[u]);
+          float xm;
+          asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(xm) : "v"(v), "s"(m));
+          x[r] = xm;
         } else {
           x[r] = e;
         }
@@ -554,6 +573,12 @@ __device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const f
       }
     }
   }
+}
+// The dV pass has no mask; the dK pass masks dS with lane masks built on
+// the scalar unit (one v_cndmask per value, no vector compare).
+template <bool kDk>
+__device__ __forceinline__ void kv_softmax(GState& st, const float* lse, const float* dd, int nq, int hh) {
+  kv_softmax_t<kDk, kDk>(st, lse, dd, nq, hh);
 }
 
 constexpr int kKvKeysPerWG = kBwdKvWaves * 32;
@@ -664,7 +689,7 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
       load_vt(dot_bh + (int64_t)js * kVtileElems, vo, obuf(j), sub);
     if (lane < 16) {
       const uint32_t r = (uint32_t)min(16 * sub + lane, nq - 1);
-      dma4((const char*)(a.lse + hb + q0), 4u * r, addr_of((const char*)(lrow(j) + 16 * sub)));
+      dma4((const char*)(a.lse2 + hb + q0), 4u * r, addr_of((const char*)(lrow(j) + 16 * sub)));
       if (kDk) dma4((const char*)(a.Dvec + hb + q0), 4u * r, addr_of((const char*)(drow(j) + 16 * sub)));
     }
   };

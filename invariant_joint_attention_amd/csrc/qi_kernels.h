@@ -97,6 +97,7 @@ struct BwdArgs {
   View<const float> o;  // FP32 pre-cast forward output
   const float* lse;  // [B,H,S]
   float* Dvec;       // [B,H,S] workspace: rowsum(dO * O)
+  float* lse2;       // [B,H,S] workspace: LSE * log2(e), for the key-side passes
   View<float> dq, dk, dv;
   int B, S, H, T_txt, T_img;
   int n_qtiles, n_ktiles;
