@@ -169,29 +169,30 @@ struct GBases {
 // 2(j%2)+1; two transposed fragments, 4 MFMAs), then score steps: with dP,
 // j = 0..15 covers head-dim chunk j/2 of 32-row block j%2 (S and dP, two
 // row fragments); without, j = 0..7 covers chunk j of both blocks (S only).
-// Each step reads two fragments, kAhead steps before its MFMAs.
-constexpr int kAhead = 2;
-using Ring = bf16x8[kAhead + 1][2];
+// Each step reads two fragments, A steps before its MFMAs (A = 2 in the dQ
+// pass, whose registers are full; 3 in the dK and dV passes).
+template <int A>
+using Ring = bf16x8[A + 1][2];
 
 // kF16 (dV pass): the gradient's A operand comes from a transposed FP16
 // tile, one ds_read_b128 per fragment instead of two transposing reads.
-template <bool kAcc, bool kS, bool kDp, bool kF16>
+template <bool kAcc, bool kS, bool kDp, bool kF16, int A>
 struct Plan {
   static constexpr int nacc = kAcc ? 8 : 0;
   static constexpr int n = nacc + (kS ? (kDp ? 16 : 8) : 0);
   static constexpr int reads(int k) { return k < n ? (k < nacc ? (kF16 ? 2 : 4) : 2) : 0; }
   static constexpr int later(int k) {  // LDS reads issued after step k's own, before its MFMAs
     int r = 0;
-    for (int i = 1; i <= kAhead; ++i) r += reads(k + i);
+    for (int i = 1; i <= A; ++i) r += reads(k + i);
     return r;
   }
 };
 
-template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
-__device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
-  using P = Plan<kAcc, kS, kDp, kF16>;
+template <bool kAcc, bool kS, bool kDp, bool kF16, int A, int k>
+__device__ __forceinline__ void g_issue(Ring<A>& f, const GBases& b) {
+  using P = Plan<kAcc, kS, kDp, kF16, A>;
   if constexpr (k < P::n) {
-    bf16x8* x = f[k % (kAhead + 1)];
+    bf16x8* x = f[k % (A + 1)];
     if constexpr (k < P::nacc) {
       constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
       if constexpr (kF16) {
@@ -213,13 +214,14 @@ __device__ __forceinline__ void g_issue(Ring& f, const GBases& b) {
   }
 }
 
-template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
-__device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
-  using P = Plan<kAcc, kS, kDp, kF16>;
+template <bool kAcc, bool kS, bool kDp, bool kF16, int A, int k>
+__device__ __forceinline__ void g_step(GState& st, Ring<A>& f, const GBases& b) {
+  using P = Plan<kAcc, kS, kDp, kF16, A>;
   if constexpr (k < P::n) {
-    g_issue<kAcc, kS, kDp, kF16, k + kAhead>(f, b);
+    g_issue<kAcc, kS, kDp, kF16, A, k + A>(f, b);
     constexpr int later = P::later(k);
-    bf16x8* x = f[k % (kAhead + 1)];
+    static_assert(later <= 15, "lgkmcnt holds at most 15");
+    bf16x8* x = f[k % (A + 1)];
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x[0]), "+v"(x[1]) : "i"(later));
     if constexpr (k < P::nacc) {
       constexpr int c2 = k >> 1, d0 = 2 * (k & 1), d1 = d0 + 1;
@@ -247,28 +249,28 @@ __device__ __forceinline__ void g_step(GState& st, Ring& f, const GBases& b) {
       st.s[1] = mfma32(x[1], st.b1[kk], kk == 0 ? z : st.s[1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    g_step<kAcc, kS, kDp, kF16, k + 1>(st, f, b);
+    g_step<kAcc, kS, kDp, kF16, A, k + 1>(st, f, b);
   }
 }
 
-template <bool kAcc, bool kS, bool kDp, bool kF16, int k>
-__device__ __forceinline__ void g_prefetch(Ring& f, const GBases& b) {
-  if constexpr (k < kAhead) {
-    g_issue<kAcc, kS, kDp, kF16, k>(f, b);
-    g_prefetch<kAcc, kS, kDp, kF16, k + 1>(f, b);
+template <bool kAcc, bool kS, bool kDp, bool kF16, int A, int k>
+__device__ __forceinline__ void g_prefetch(Ring<A>& f, const GBases& b) {
+  if constexpr (k < A) {
+    g_issue<kAcc, kS, kDp, kF16, A, k>(f, b);
+    g_prefetch<kAcc, kS, kDp, kF16, A, k + 1>(f, b);
   }
 }
 
-template <bool kAcc, bool kS, bool kDp, bool kF16 = false>
+template <bool kAcc, bool kS, bool kDp, bool kF16 = false, int A = 2>
 __device__ __forceinline__ void g_matrix(GState& st, GBases b) {
-  Ring f;
+  Ring<A> f;
   // opaque copies keep the per-step address XORs inside their steps
   asm volatile("" : "+v"(b.t), "+v"(b.r1), "+v"(b.r2));
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
-  g_prefetch<kAcc, kS, kDp, kF16, 0>(f, b);
+  g_prefetch<kAcc, kS, kDp, kF16, A, 0>(f, b);
   __builtin_amdgcn_sched_barrier(0);
-  g_step<kAcc, kS, kDp, kF16, 0>(st, f, b);
+  g_step<kAcc, kS, kDp, kF16, A, 0>(st, f, b);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -726,7 +728,7 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
     b0.t = 0;
     b0.r1 = row_base(addr_of(qbuf(0)), lane);
     b0.r2 = row_base(addr_of(obuf(0)), lane);
-    g_matrix<false, true, kDk>(st, b0);
+    g_matrix<false, true, kDk, false, 3>(st, b0);
   }
 #pragma clang loop unroll(disable)
   for (int t = 0; t + 1 < nt; ++t) {
@@ -737,13 +739,13 @@ __device__ __forceinline__ void kv_pass(const BwdArgs& a, char* smem, int g) {
       load_g0(t + 3);
     kv_softmax<kDk>(st, lrow(t), drow(t), nq_of(t), hh);
     group_barrier<0, 4>(grp);  // B_t for group 0: tile t+3, issued just now, may stay in flight
-    g_matrix<true, true, kDk, !kDk>(st, bases(t, true));
+    g_matrix<true, true, kDk, !kDk, 3>(st, bases(t, true));
   }
   // the last tile
   group_barrier<1, 0>(grp);
   kv_softmax<kDk>(st, lrow(nt - 1), drow(nt - 1), nq_of(nt - 1), hh);
   group_barrier<0, 0>(grp);
-  g_matrix<true, false, kDk, !kDk>(st, bases(nt - 1, false));
+  g_matrix<true, false, kDk, !kDk, 3>(st, bases(nt - 1, false));
 
   if (kvalid) {
     // dK: times 1/sqrt(128); dV: times 2^-e, undoing dO's power-of-two scale (exact)
