@@ -1172,7 +1172,7 @@ const char* qi_trace(void) {
              "\"bwd_D\":\"rowsum(dO*O) from the fp32 forward O\","
              "\"reference_max_threshold_log2\":8,"
              "\"ds_split\":\"hi=bf16(dS), lo=bf16(dS-hi), accumulated hi then lo (dQ, dK)\","
-             "\"dv_operands\":\"P fp16 RNE, dO fp16 RNE of dO*2^e per (b,h) (e from its max|dO|, taken in the dQ pass), dV=acc*2^-e\","
+             "\"dv_operands\":\"P fp16 RNE, dO fp16 RNE of dO*2^e per (b,h) (e from its max|dO|, taken by the preparation kernel), dV=acc*2^-e\","
              "\"rms_sum_tree\":\"8 sequential per lane, xor 8,4,2,1\","
              "\"dgain_fold\":\"chunks ascending per sample, then samples ascending\"},"
              "\"free\":[\"rows per workgroup\",\"grid order / XCD mapping\",\"LDS layout\",\"prefetch depth\"],"
