@@ -496,7 +496,7 @@ int launch_prologue_bwd(const qi_geom* g, const qi_bshd x[2], const float* const
   hipLaunchKernelGGL(qknorm_rope_bwd_kernel, dim3(Lw.n_chunks, g->B, 2), dim3(256), 0, st, pp);
   int rc = launched("qknorm_rope_bwd_kernel");
   if (rc) return rc;
-  hipLaunchKernelGGL(dgain_fold_kernel, dim3(g->gain_streams, 2), dim3(kHeadDim), 0, st, fp);
+  hipLaunchKernelGGL(dgain_fold_kernel, dim3(g->gain_streams, 2), dim3(4 * kHeadDim), 0, st, fp);
   return launched("dgain_fold_kernel");
 }
 

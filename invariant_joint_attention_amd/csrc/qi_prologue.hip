@@ -246,10 +246,17 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(PrologueBwdPair p)
 
 // Fold the chunk partials of each sample and gain set in ascending chunk
 // order, then (one thread per channel and set) the per-sample results in
-// ascending b.  Grid: (gain_streams), block: 128 x B-independent loop.
-__global__ __launch_bounds__(128) void dgain_fold_kernel(DgainFoldPair p) {
+// ascending b.  Grid: (gain_streams, 2 gains); block: 4 x 128 threads.
+// The adds are one thread per channel, in chunk order; all 512 threads load
+// the partials into LDS 64 chunks at a time, and the next batch's loads are
+// in flight while the current batch is added, so the chain waits on memory
+// about once per sample instead of once per batch.
+constexpr int kFoldBatch = 64;
+constexpr int kFoldThreads = 4 * kHeadDim;
+__global__ __launch_bounds__(kFoldThreads) void dgain_fold_kernel(DgainFoldPair p) {
   const DgainFoldArgs a = blockIdx.y ? p.t[1] : p.t[0];  // Q's or K's gain (uniform)
-  const int set = blockIdx.x, cc = threadIdx.x;
+  const int set = blockIdx.x, tid = threadIdx.x, cc = tid & (kHeadDim - 1), grp = tid >> 7;
+  __shared__ float buf[kFoldBatch][kHeadDim];
   int k0, k1;
   if (a.gain_streams == 2) {
     k0 = set == 0 ? 0 : a.n_txt_chunks;
@@ -260,23 +267,39 @@ __global__ __launch_bounds__(128) void dgain_fold_kernel(DgainFoldPair p) {
   }
   float tot = 0.f;
   for (int b = 0; b < a.B; ++b) {
-    // The adds run in ascending chunk order; the loads of a batch of 32
-    // chunks are all issued before its adds, so the chain waits on memory
-    // once per batch instead of once per chunk.
     const float* src = a.partials + (int64_t)b * a.n_chunks * kHeadDim + cc;
+    float x[kFoldBatch / 4];  // chunks base + 4j + grp of the batch this thread loads
+    auto fetch = [&](int base) {
+#pragma unroll
+      for (int j = 0; j < kFoldBatch / 4; ++j) {
+        const int k = base + 4 * j + grp;
+        x[j] = k < k1 ? src[(int64_t)k * kHeadDim] : 0.f;
+      }
+    };
+    fetch(k0);
     float v = 0.f;
-    for (int kk = k0; kk < k1; kk += 32) {
-      float x[32];
+    for (int base = k0; base < k1; base += kFoldBatch) {
+      __syncthreads();  // the previous batch's adds are done with buf
 #pragma unroll
-      for (int j = 0; j < 32; ++j) x[j] = kk + j < k1 ? src[(int64_t)(kk + j) * kHeadDim] : 0.f;
+      for (int j = 0; j < kFoldBatch / 4; ++j) buf[4 * j + grp][cc] = x[j];
+      __syncthreads();
+      if (base + kFoldBatch < k1) fetch(base + kFoldBatch);
+      if (tid < kHeadDim) {  // the batch's reads all issued, then the adds in chunk order
+        const int n = min(kFoldBatch, k1 - base);
+        float y[kFoldBatch];
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
-        if (kk + j < k1) v = v + x[j];
+        for (int j = 0; j < kFoldBatch; ++j) y[j] = buf[j][cc];
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j)
+          if (j < n) v = v + y[j];
+      }
     }
-    a.dg_ps[((int64_t)b * a.gain_streams + set) * kHeadDim + cc] = v;
-    tot = tot + v;
+    if (tid < kHeadDim) {
+      a.dg_ps[((int64_t)b * a.gain_streams + set) * kHeadDim + cc] = v;
+      tot = tot + v;
+    }
   }
-  if (a.dg) a.dg[set * kHeadDim + cc] = tot;
+  if (tid < kHeadDim && a.dg) a.dg[set * kHeadDim + cc] = tot;
 }
 
 }  // namespace qi
