@@ -12,7 +12,7 @@ import torch
 
 import workloads
 from oracle import Oracle, fold_batch
-from parity import abs_check, f64, mixed_check
+from parity import DEBUG_ATOL, ParityStats, abs_check, f64, mixed_check
 
 qi = pytest.importorskip("invariant_joint_attention_amd")
 
@@ -87,8 +87,12 @@ def test_prologue_full(orc, cfg):
     y = qi.qknorm_rope(g["q"], g["g_q"], geo, out_f32=yf)
     torch.cuda.synchronize()
     ref = orc.qknorm_rope(orc.widen(workloads.bits(inp["q"])), inp["g_q"].numpy(), wl.T_txt, wl.h, wl.w)
-    abs_check(yf, ref, "q' fp32")
-    mixed_check(y, ref, "q' bf16")
+    s32 = ParityStats(f"{cfg} q' (FP32)", rtol=0.0, atol=DEBUG_ATOL)
+    s16 = ParityStats(f"{cfg} q' (BF16)")
+    abs_check(yf, ref, "q' fp32", stats=s32)
+    mixed_check(y, ref, "q' bf16", stats=s16)
+    print(s32.line(), flush=True)
+    print(s16.line(), flush=True)
 
 
 # ------------------------------------------------------------------- forward
@@ -131,12 +135,15 @@ def test_forward_full_every_element(orc, cfg):
     q, k, o, lse, _ = _fwd_all(g, geo)
     qn, kn, on, ln = f64(q), f64(k), f64(o), f64(lse)
     vn = f64(inp["v"].float())
+    so, sl = ParityStats(f"{cfg} O (BF16)"), ParityStats(f"{cfg} LSE (FP32)", rtol=0.0, atol=DEBUG_ATOL)
     for b in range(wl.B):
         for h in range(wl.H):
             ro, rl = orc.attn_fwd_bh(qn[b, :, h], kn[b, :, h], vn[b, :, h], wl.T_txt, wl.txt_len[b], 0, wl.S)
-            mixed_check(on[b, :, h], ro, f"O b{b} h{h}")
-            abs_check(ln[b, h], rl, f"LSE b{b} h{h}")
+            mixed_check(on[b, :, h], ro, f"O b{b} h{h}", stats=so, where=(b, h))
+            abs_check(ln[b, h], rl, f"LSE b{b} h{h}", stats=sl, where=(b, h))
         print(f"{cfg}: sample {b}, {wl.H} heads x {wl.S} rows checked", flush=True)
+    print(so.line(), flush=True)
+    print(sl.line(), flush=True)
 
 
 def test_forward_constant_v_and_scaling():
@@ -270,11 +277,14 @@ def test_backward_full_config_every_element(orc):
     dqp, dkp, dv = orc.attn_bwd(f64(q), f64(k), f64(inp["v"].float()), f64(inp["dO"].float()), txt_len, wl.T_txt)
     dq, dgq = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["q"])), inp["g_q"].numpy(), dqp, wl.T_txt, wl.h, wl.w)
     dk, dgk = orc.qknorm_rope_bwd(orc.widen(workloads.bits(inp["k"])), inp["g_k"].numpy(), dkp, wl.T_txt, wl.h, wl.w)
+    st = {n: ParityStats(f"1024sq_bwd B=2 {n} (FP32)") for n in ("dv", "dq", "dk", "dgain_q", "dgain_k")}
     for b in range(2):
-        mixed_check(r["dv"][b], dv[b], f"dv sample {b}")
-        mixed_check(r["dq"][b], dq[b], f"dq sample {b}")
-        mixed_check(r["dk"][b], dk[b], f"dk sample {b}")
-    mixed_check(r["dgain_q_ps"], dgq, "dgain_q per sample")
-    mixed_check(r["dgain_k_ps"], dgk, "dgain_k per sample")
+        mixed_check(r["dv"][b], dv[b], f"dv sample {b}", stats=st["dv"], where=(b,))
+        mixed_check(r["dq"][b], dq[b], f"dq sample {b}", stats=st["dq"], where=(b,))
+        mixed_check(r["dk"][b], dk[b], f"dk sample {b}", stats=st["dk"], where=(b,))
+    mixed_check(r["dgain_q_ps"], dgq, "dgain_q per sample", stats=st["dgain_q"])
+    mixed_check(r["dgain_k_ps"], dgk, "dgain_k per sample", stats=st["dgain_k"])
     mixed_check(r["dgain_q"], fold_batch(dgq), "dgain_q folded")
     mixed_check(r["dgain_k"], fold_batch(dgk), "dgain_k folded")
+    for v in st.values():
+        print(v.line(), flush=True)
