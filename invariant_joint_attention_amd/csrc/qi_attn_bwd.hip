@@ -336,16 +336,25 @@ __global__ __launch_bounds__(kBwdDqWaves * 64) void attn_bwd_prep_kernel(BwdArgs
   const bool qvalid = qrow < a.S;
   float dpart = 0.f;
   uint32_t amax = 0;  // max |dO| of this lane's values, as BF16 magnitude bits (ordered like the values)
+  // All 24 loads first, branch-free (rows past S read row S-1, and a bit
+  // mask turns their values into +0), so none of them waits for another.
+  const int qr = qvalid ? qrow : a.S - 1;
+  const uint32_t vm = qvalid ? ~0u : 0u;
+  u32x4 zdv[8];
+  f32x4 o0v[8], o1v[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    u32x4 zd = {0u, 0u, 0u, 0u};
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-    if (qvalid) {
-      zd = *(const u32x4*)(a.dO.row(b, qrow, h) + 16 * kk + 8 * hh);
-      const float* orow = a.o.row(b, qrow, h) + 16 * kk + 8 * hh;
-      o0 = *(const f32x4*)orow;
-      o1 = *(const f32x4*)(orow + 4);
-    }
+    zdv[kk] = *(const u32x4*)(a.dO.row(b, qr, h) + 16 * kk + 8 * hh);
+    const float* orow = a.o.row(b, qr, h) + 16 * kk + 8 * hh;
+    o0v[kk] = *(const f32x4*)orow;
+    o1v[kk] = *(const f32x4*)(orow + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const u32x4 zd = zdv[kk] & vm;
+    const f32x4 o0 = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, o0v[kk]) & vm);
+    const f32x4 o1 = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, o1v[kk]) & vm);
     const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
