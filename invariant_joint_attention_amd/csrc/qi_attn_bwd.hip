@@ -401,13 +401,6 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
     st.b1[kk] = __builtin_bit_cast(bf16x8, zq);
     st.b2[kk] = __builtin_bit_cast(bf16x8, zd);
   }
-  st.lse2 = INFINITY;
-  st.D = 0.f;
-  if (qvalid) {
-    const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
-    st.lse2 = a.lse[li] * kLog2e;
-    st.D = a.Dvec[li];
-  }
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -462,6 +455,16 @@ __device__ __forceinline__ void dq_pass(const BwdArgs& a, char* smem, int g) {
     for (int j = 0; j < 3 && j < nt; ++j) load_v(j);
   } else {
     for (int j = 0; j < 3 && j < nt; ++j) load_k(j);
+  }
+  // The row's LSE and D after the first tiles' loads, so that their wait
+  // is the one before the first barrier (not a wait of its own before the
+  // tile loads are issued).
+  st.lse2 = INFINITY;
+  st.D = 0.f;
+  if (qvalid) {
+    const int64_t li = ((int64_t)b * a.H + h) * a.S + qrow;
+    st.lse2 = a.lse[li] * kLog2e;
+    st.D = a.Dvec[li];
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   bar();
