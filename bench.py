@@ -26,8 +26,8 @@ a backward workload `fwd_bwd_step` adds the backward's 10 * D * H * sum_b S * K_
 to the count over the same step time.
 The K timed steps run back to back between one pair of HIP events and the
 host clock (no event inside the region).  The attention-forward call is then
-timed alone on the launch stream: K back-to-back calls between one event
-pair, five repeats (by default one launch of the attention kernel; with
+timed alone on the launch stream: max(K, 100) back-to-back calls between one
+event pair, five repeats (by default one launch of the attention kernel; with
 --separate-prologue the V tile pass and the attention kernel); that time
 gives the roofline fraction against the MI355X dense BF16 MFMA peak
 (2.5 PFLOP/s).  The other measurements of the line (the 1024^2 backward, the
@@ -285,10 +285,11 @@ def main():
     # repeats (mean of the repeats for the roofline; median and min beside
     # it); the prologue (and backward) the same way.
     j_fwd = names.index("fwd")
-    fwd_rep = [region(runs[j_fwd], args.steps) for _ in range(5)]
+    n_alone = max(args.steps, 100)  # at least 100 back-to-back calls per repeat, whatever K is
+    fwd_rep = [region(runs[j_fwd], n_alone) for _ in range(5)]
     fwd_ms = float(np.mean(fwd_rep))
     fwd_t = fwd_rep
-    pro_ms = region(runs[names.index("pro")], args.steps)
+    pro_ms = region(runs[names.index("pro")], n_alone)
     bwd_ms = region(runs[names.index("bwd")], max(1, args.steps // 4)) if wl.backward else 0.0
     torch.cuda.synchronize()
     clock_before, clock_after = clock.mhz(0), clock.mhz(1)
@@ -359,7 +360,7 @@ def main():
         "env": env,
         "sha256": {"inputs": in_sha, "outputs_o_lse": out_sha},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "attn_fwd": {"timed": f"5 repeats of {args.steps} back-to-back calls, one event pair each, after the "
+        "attn_fwd": {"timed": f"5 repeats of {n_alone} back-to-back calls, one event pair each, after the "
                               "timed steps",
                      "ms": round(fwd_ms, 4), "median_ms": round(float(np.median(fwd_t)), 4),
                      "min_ms": round(float(np.min(fwd_t)), 4), "max_ms": round(float(np.max(fwd_t)), 4),
@@ -374,7 +375,7 @@ def main():
                                 "per SIMD running BF16 MFMAs for ~30 us, sampled just before and just after "
                                 "the timed steps"},
         "prologue": {"calls": "qi_qknorm_rope x 2" if args.separate_prologue else "qi_qkv_prologue (Q, K, V tiles)",
-                     "timed": f"{args.steps} back-to-back calls after the timed steps", "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
+                     "timed": f"{n_alone} back-to-back calls after the timed steps", "ms": round(pro_ms, 4), "bytes": pro_bytes, "gbps": round(pro_bytes / (pro_ms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
         "launch": "hip_graph_replay" if args.graph else "eager",
